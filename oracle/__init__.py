@@ -1,0 +1,149 @@
+"""fp64 CPU oracle for exact attention -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  The library under test never does.
+
+The arithmetic lives in ``oracle.c`` (plain fp64 C, OpenMP over rows); this
+module compiles it with gcc when no build is present and marshals numpy
+arrays of bf16 bit patterns (uint16) into it.  Nothing here is shared with
+the HIP library.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+CAUSAL, WINDOW, DOCS, SOFTCAP = 1, 2, 4, 8
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+
+def build(force: bool = False) -> str:
+    """Compile oracle.c into liboracle.so (gcc, -O2, OpenMP, IEEE math)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp"
+        subprocess.check_call(["gcc", "-O2", "-fopenmp", "-fPIC", "-shared",
+                               "-std=c99", "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        build()
+        lib = ctypes.CDLL(_LIB)
+        P = ctypes.c_void_p
+        i32, i64, f64 = ctypes.c_int, ctypes.c_int64, ctypes.c_double
+        lib.oracle_fwd.restype = i32
+        lib.oracle_fwd.argtypes = [P, P, P, P, P, P, i32, i32, i32, i32, i32,
+                                   i32, i64, i64, f64, P, i32, f64, i64, P, P,
+                                   P, P]
+        lib.oracle_decode.restype = i32
+        lib.oracle_decode.argtypes = [P, P, P, P, P, P, i32, i32, i32, i32,
+                                      i32, f64, P, P]
+        lib.oracle_threads.restype = i32
+        lib.oracle_threads.argtypes = []
+        _lib = lib
+    return _lib
+
+
+def threads() -> int:
+    return _load().oracle_threads()
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _strides(a: np.ndarray) -> np.ndarray:
+    """(b, h, n) element strides of a 4-D array with unit last stride."""
+    if a.ndim != 4 or a.strides[3] != a.itemsize:
+        raise ValueError("expected a 4-D array with contiguous last axis")
+    return np.array([s // a.itemsize for s in a.strides[:3]], dtype=np.int64)
+
+
+def fwd(q, k, v, *, scale, causal=False, window=None, doc_offsets=None,
+        softcap=None, rows=None, want_probs=False):
+    """Exact attention, fp64.
+
+    q [B,Hq,N,d], k/v [B,Hkv,N,d]: uint16 bf16 bit patterns.
+    window: None, an int w (|i-j| <= w) or a pair (left, right).
+    doc_offsets: int32 [B][max_docs+1] padded with N, or None.
+    rows: None for every row, else int array [n,3] of (b, h, i).
+    Returns (O [..., d] float64, LSE float64[, P]) shaped [B,Hq,N,...] for
+    all rows, or [n, ...] for selected rows.
+    """
+    lib = _load()
+    for a in (q, k, v):
+        if a.dtype != np.uint16:
+            raise TypeError("oracle inputs are bf16 bit patterns (uint16)")
+    B, Hq, N, d = q.shape
+    Hkv = k.shape[1]
+    flags = 0
+    wl = wr = 0
+    if causal:
+        flags |= CAUSAL
+    if window is not None:
+        flags |= WINDOW
+        wl, wr = (window, window) if np.isscalar(window) else window
+    offs = None
+    doc_stride = 0
+    if doc_offsets is not None:
+        flags |= DOCS
+        offs = np.ascontiguousarray(doc_offsets, dtype=np.int32)
+        doc_stride = offs.shape[1]
+    cap = 0.0
+    if softcap is not None:
+        flags |= SOFTCAP
+        cap = float(softcap)
+    if rows is None:
+        nrows = B * Hq * N
+        rows_arr = None
+    else:
+        rows_arr = np.ascontiguousarray(rows, dtype=np.int32).reshape(-1, 3)
+        nrows = rows_arr.shape[0]
+    o = np.empty((nrows, d), dtype=np.float64)
+    lse = np.empty(nrows, dtype=np.float64)
+    p = np.empty((nrows, N), dtype=np.float64) if want_probs else None
+    qs, ks, vs = _strides(q), _strides(k), _strides(v)
+    rc = lib.oracle_fwd(_ptr(q), _ptr(qs), _ptr(k), _ptr(ks), _ptr(v), _ptr(vs),
+                        B, Hq, Hkv, N, d, flags, int(wl), int(wr), cap,
+                        _ptr(offs), doc_stride, float(scale), nrows,
+                        _ptr(rows_arr), _ptr(o), _ptr(lse), _ptr(p))
+    if rc != 0:
+        raise ValueError("oracle_fwd rejected its arguments")
+    if rows is None:
+        o = o.reshape(B, Hq, N, d)
+        lse = lse.reshape(B, Hq, N)
+        if p is not None:
+            p = p.reshape(B, Hq, N, N)
+    return (o, lse, p) if want_probs else (o, lse)
+
+
+def decode(q, kc, vc, lens, *, scale):
+    """One query per (b, hq) against cache keys j < lens[b]; fp64.
+
+    q [B,Hq,d], kc/vc [B,Hkv,T,d] uint16 bf16 bits, lens int32 [B].
+    Returns (O [B,Hq,d], LSE [B,Hq]).
+    """
+    lib = _load()
+    B, Hq, d = q.shape
+    Hkv, T = kc.shape[1], kc.shape[2]
+    q = np.ascontiguousarray(q)
+    lens = np.ascontiguousarray(lens, dtype=np.int32)
+    o = np.empty((B, Hq, d), dtype=np.float64)
+    lse = np.empty((B, Hq), dtype=np.float64)
+    ks, vs = _strides(kc), _strides(vc)
+    rc = lib.oracle_decode(_ptr(q), _ptr(kc), _ptr(ks), _ptr(vc), _ptr(vs),
+                           _ptr(lens), B, Hq, Hkv, T, d, float(scale), _ptr(o),
+                           _ptr(lse))
+    if rc != 0:
+        raise ValueError("oracle_decode rejected its arguments")
+    return o, lse

@@ -1,0 +1,86 @@
+"""Pure-Python brute-force attention for tiny shapes (checks the C oracle).
+
+Written independently of ``oracle/oracle.c``: masks are evaluated from
+explicit per-token document ids, the soft cap uses ``math.tanh``, and every
+sum is a plain Python loop.  Only for N <= ~16, d <= ~8.
+"""
+import math
+
+
+def bf16_to_float(bits):
+    import struct
+    return struct.unpack("<f", struct.pack("<I", int(bits) << 16))[0]
+
+
+def doc_ids_from_offsets(offsets, N):
+    ids = [0] * N
+    doc = -1
+    starts = set(int(x) for x in offsets if int(x) < N)
+    for i in range(N):
+        if i in starts:
+            doc += 1
+        ids[i] = doc
+    return ids
+
+
+def attention(q, k, v, scale, causal=False, window=None, doc_offsets=None,
+              softcap=None):
+    """q [B][Hq][N][d], k/v [B][Hkv][N][d] nested lists of floats.
+
+    Returns O [B][Hq][N][d], LSE [B][Hq][N] as nested lists of floats."""
+    B, Hq, N, d = len(q), len(q[0]), len(q[0][0]), len(q[0][0][0])
+    Hkv = len(k[0])
+    group = Hq // Hkv
+    if window is None:
+        wl = wr = None
+    elif isinstance(window, int):
+        wl = wr = window
+    else:
+        wl, wr = window
+    O = []
+    L = []
+    for b in range(B):
+        ids = doc_ids_from_offsets(doc_offsets[b], N) if doc_offsets is not None else None
+        Ob, Lb = [], []
+        for h in range(Hq):
+            hk = h // group
+            Oh, Lh = [], []
+            for i in range(N):
+                scores = []
+                for j in range(N):
+                    ok = True
+                    if causal and j > i:
+                        ok = False
+                    if wl is not None and not (i - wl <= j <= i + wr):
+                        ok = False
+                    if ids is not None and ids[i] != ids[j]:
+                        ok = False
+                    if not ok:
+                        continue
+                    dot = 0.0
+                    for t in range(d):
+                        dot += q[b][h][i][t] * k[b][hk][j][t]
+                    s = dot * scale
+                    if softcap is not None:
+                        s = softcap * math.tanh(s / softcap)
+                    scores.append((j, s))
+                if not scores:
+                    Oh.append([0.0] * d)
+                    Lh.append(-math.inf)
+                    continue
+                mx = max(s for _, s in scores)
+                den = 0.0
+                for _, s in scores:
+                    den += math.exp(s - mx)
+                out = [0.0] * d
+                for j, s in scores:
+                    w = math.exp(s - mx) / den
+                    for t in range(d):
+                        out[t] += w * v[b][hk][j][t]
+                Oh.append(out)
+                Lh.append(mx + math.log(den))
+            Ob.append(Oh)
+            Lb.append(Lh)
+        O.append(Ob)
+        L.append(Lb)
+    return O, L
