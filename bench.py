@@ -1,0 +1,363 @@
+#!/usr/bin/env python3
+"""Benchmark of the exact-attention hot path on one MI355X.
+
+Headline (``value``): forward-attention throughput in TFLOP/s on the causal
+MHA workload B=8, H=32, N=4096, d=128 (bf16 inputs drawn N(0,1)*0.5 from a
+seed, scale 1/sqrt(128)).  One timed step is one ``attn_fwd`` call that
+builds the block mask in its workspace and runs the forward kernel, i.e. the
+whole forward path.  FLOPs count 4*d per visible (query, key) pair.
+
+The same JSON line also carries:
+  roofline      the forward kernel alone (prebuilt block mask), timed with
+                HIP events on the stream it is launched on, against the bf16
+                dense MFMA peak;
+  decode        split-KV decode (split + combine kernels) on B=16, 32 query
+                heads over 8 KV heads, T=32768, lens U[1024, 32768], chunk
+                1024: HBM GB/s of the algorithmic K/V bytes, against 8 TB/s;
+  configs       every workload's time and throughput;
+  cpu_baseline  the fp64 oracle timed on the host cores on a bounded sample
+                of the headline workload (rows of a few heads).
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+                       [--configs 1,2,3,4,5]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import attn_inputs as gen  # noqa: E402
+
+METRIC = "fwd attention TFLOPS & % bf16 MFMA peak; decode split-KV HBM GB/s"
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
+HBM_PEAK_GBS = 8000.0           # MI355X HBM3E
+
+
+# ---------------------------------------------------------------------------
+# Algorithmic work accounting (host, closed forms from the mask intervals).
+# ---------------------------------------------------------------------------
+def row_intervals(kind: str, N: int, *, window=None, doc_offsets=None):
+    """Visible key interval [lo, hi] of every query row (one batch row)."""
+    i = np.arange(N, dtype=np.int64)
+    lo = np.zeros(N, np.int64)
+    hi = np.full(N, N - 1, np.int64)
+    if kind in ("causal", "docs_causal"):
+        hi = np.minimum(hi, i)
+    if kind == "window_softcap":
+        lo = np.maximum(lo, i - window)
+        hi = np.minimum(hi, i + window)
+    if doc_offsets is not None:
+        offs = np.asarray(doc_offsets, np.int64)
+        idx = np.searchsorted(offs, i, side="right") - 1
+        lo = np.maximum(lo, offs[idx])
+        hi = np.minimum(hi, offs[idx + 1] - 1)
+    return lo, hi
+
+
+def visible_pairs(kind: str, B: int, N: int, *, window=None, doc_rows=None) -> int:
+    """Visible (query, key) pairs of one head, summed over the batch."""
+    total = 0
+    for b in range(B):
+        lo, hi = row_intervals(kind, N, window=window,
+                               doc_offsets=None if doc_rows is None else doc_rows[b])
+        total += int(np.maximum(hi - lo + 1, 0).sum())
+    return total
+
+
+def fwd_flops(pairs_per_head: int, H: int, d: int) -> float:
+    """QK^T and PV: 2*d each per visible pair."""
+    return 4.0 * d * pairs_per_head * H
+
+
+def score_matrix_bytes(B, H, N, elem_bytes=2) -> int:
+    """Bytes of a materialised [B, H, N, N] score matrix."""
+    return B * H * N * N * elem_bytes
+
+
+def kv_cache_bytes(B, Hkv, T, d, elem_bytes=2) -> int:
+    """Bytes of a K and V cache pair [B, Hkv, T, d]."""
+    return 2 * B * Hkv * T * d * elem_bytes
+
+
+def decode_bytes(lens, Hkv, Hq, d) -> int:
+    """Algorithmic HBM bytes of one decode step: the valid K and V rows, the
+    queries, the outputs and the LSE (the partials are workspace traffic and
+    are not counted)."""
+    lens = np.asarray(lens, np.int64)
+    B = len(lens)
+    return int(lens.sum()) * Hkv * d * 2 * 2 + B * Hq * d * 2 * 2 + B * Hq * 4 + B * 4
+
+
+def fwd_io_bytes(B, Hq, Hkv, N, d) -> int:
+    """Compulsory HBM bytes of the forward pass: Q, K, V read once, O and
+    LSE written once."""
+    return (B * Hq * N * d + 2 * B * Hkv * N * d) * 2 + B * Hq * N * d * 2 + B * Hq * N * 4
+
+
+# ---------------------------------------------------------------------------
+# Workloads
+# ---------------------------------------------------------------------------
+def fwd_workload(cfg_id: int, device):
+    import torch
+    c = gen.CONFIGS[cfg_id]
+    docs = c["kind"] == "docs_causal"
+    q, k, v, doc_rows = gen.fwd_inputs(c["seed"], c["B"], c["Hq"], c["Hkv"], c["N"], c["d"],
+                                       c["factor"], docs=docs)
+    w = dict(cfg=c, q_bits=q, k_bits=k, v_bits=v, doc_rows=doc_rows)
+    w["q"], w["k"], w["v"] = (to_dev(x, device) for x in (q, k, v))
+    w["scale"] = 1.0 / math.sqrt(c["d"])
+    kw_dev, kw_ref = {}, {}
+    if c["kind"] in ("causal", "docs_causal"):
+        kw_dev["causal"] = kw_ref["causal"] = True
+    if c["kind"] == "window_softcap":
+        kw_dev["window"] = kw_ref["window"] = c["window"]
+        kw_dev["softcap"] = kw_ref["softcap"] = c["softcap"]
+    if docs:
+        padded, _ = gen.pad_offsets(doc_rows, c["N"])
+        kw_ref["doc_offsets"] = padded
+        kw_dev["doc_offsets"] = torch.from_numpy(padded).to(device)
+    w["kw_dev"], w["kw_ref"] = kw_dev, kw_ref
+    w["pairs_per_head"] = visible_pairs(c["kind"], c["B"], c["N"], window=c.get("window"),
+                                        doc_rows=doc_rows)
+    w["flops"] = fwd_flops(w["pairs_per_head"], c["Hq"], c["d"])
+    return w
+
+
+def decode_workload(device):
+    import torch
+    c = gen.CONFIGS[5]
+    q, kc, vc, lens = gen.decode_inputs(c["seed"], c["B"], c["Hq"], c["Hkv"], c["T"], c["d"])
+    w = dict(cfg=c, q_bits=q, k_bits=kc, v_bits=vc, lens=lens)
+    w["q"], w["k"], w["v"] = (to_dev(x, device) for x in (q, kc, vc))
+    w["lens_dev"] = torch.from_numpy(lens).to(device)
+    w["scale"] = 1.0 / math.sqrt(c["d"])
+    w["bytes"] = decode_bytes(lens, c["Hkv"], c["Hq"], c["d"])
+    return w
+
+
+def to_dev(bits, device):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(device)
+
+
+# ---------------------------------------------------------------------------
+# Timing
+# ---------------------------------------------------------------------------
+def time_launches(fn, steps: int, warmup: int):
+    """Average ms per call: warmup calls, then `steps` calls between HIP events
+    recorded on the current stream (the stream the library launches on)."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(steps):
+        fn()
+    stop.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(stop) / steps
+
+
+def time_each(fn, steps: int):
+    """Per-call ms (events around every call) for median/min/p90."""
+    import torch
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    for a, b in evs:
+        a.record()
+        fn()
+        b.record()
+    torch.cuda.synchronize()
+    t = np.array([a.elapsed_time(b) for a, b in evs])
+    return dict(median_ms=float(np.median(t)), min_ms=float(t.min()),
+                p90_ms=float(np.percentile(t, 90)))
+
+
+def bench_fwd(ea, w, steps, warmup):
+    import torch
+    c = w["cfg"]
+    spec = ea.MaskSpec(**w["kw_dev"])
+    B, N = c["B"], c["N"]
+    o = torch.empty((B, c["Hq"], N, c["d"]), dtype=torch.bfloat16, device=w["q"].device)
+    lse = torch.empty((B, c["Hq"], N), dtype=torch.float32, device=w["q"].device)
+    bm = ea.mask_build(spec, B, N)
+
+    def step_with_mask_build():
+        ea.fwd(w["q"], w["k"], w["v"], spec=spec, scale=w["scale"], out=o, lse=lse)
+
+    def kernel_only():
+        ea.fwd(w["q"], w["k"], w["v"], spec=spec, scale=w["scale"], block_mask=bm, out=o, lse=lse)
+
+    def mask_only():
+        ea.mask_build(spec, B, N)
+
+    ms_step = time_launches(step_with_mask_build, steps, warmup)
+    ms_kernel = time_launches(kernel_only, steps, warmup)
+    dist = time_each(kernel_only, max(steps, 20))
+    ms_mask = time_launches(mask_only, max(steps // 2, 5), 2)
+    return dict(ms_step=ms_step, ms_kernel=ms_kernel, ms_mask_build=ms_mask, dist=dist,
+                tflops_step=w["flops"] / (ms_step * 1e-3) / 1e12,
+                tflops_kernel=w["flops"] / (ms_kernel * 1e-3) / 1e12)
+
+
+def bench_decode(ea, w, steps, warmup):
+    import torch
+    c = w["cfg"]
+    o = torch.empty((c["B"], c["Hq"], c["d"]), dtype=torch.bfloat16, device=w["q"].device)
+    lse = torch.empty((c["B"], c["Hq"]), dtype=torch.float32, device=w["q"].device)
+    ws = torch.empty(ea.decode_workspace_bytes(c["B"], c["Hq"], c["T"], c["d"], c["chunk"]),
+                     dtype=torch.uint8, device=w["q"].device)
+
+    def step():
+        ea.decode(w["q"], w["k"], w["v"], w["lens_dev"], scale=w["scale"], chunk=c["chunk"],
+                  out=o, lse=lse, workspace=ws)
+
+    ms = time_launches(step, steps, warmup)
+    dist = time_each(step, max(steps, 20))
+    return dict(ms=ms, dist=dist, gbs=w["bytes"] / (ms * 1e-3) / 1e9)
+
+
+def cpu_baseline(w, target_s=15.0):
+    """The fp64 oracle on whole heads of batch row 0 of the workload, timed on
+    the host cores; throughput in the metric's unit (TFLOP/s)."""
+    import oracle
+    c = w["cfg"]
+    N = c["N"]
+    lo, hi = row_intervals(c["kind"], N, window=c.get("window"))
+    pairs_head = int(np.maximum(hi - lo + 1, 0).sum())
+    # one head first, to size the sample
+    heads = 1
+    t0 = time.perf_counter()
+    rows = np.array([(0, 0, i) for i in range(N)], np.int32)
+    oracle.fwd(w["q_bits"], w["k_bits"], w["v_bits"], scale=w["scale"], rows=rows, **w["kw_ref"])
+    t1 = time.perf_counter() - t0
+    more = int(max(0, min(c["Hq"] - 1, round(target_s / max(t1, 1e-3)) - 1)))
+    if more:
+        rows = np.array([(0, h, i) for h in range(1, 1 + more) for i in range(N)], np.int32)
+        t0 = time.perf_counter()
+        oracle.fwd(w["q_bits"], w["k_bits"], w["v_bits"], scale=w["scale"], rows=rows,
+                   **w["kw_ref"])
+        t1 += time.perf_counter() - t0
+        heads += more
+    flops = fwd_flops(pairs_head, heads, c["d"])
+    return {"value": flops / t1 / 1e12, "unit": "TFLOP/s", "cores": oracle.threads(),
+            "kind": "oracle",
+            "sample": f"all {N} rows of {heads} head(s) of batch row 0 of {c['name']} "
+                      f"({flops / 1e9:.1f} GFLOP, {t1:.1f} s wall)"}
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--configs", default="1,2,3,4,5")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args(argv)
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: the forward and decode kernels run on a single "
+              "MI355X and no multi-GPU path is built (use --gpus 1).", file=sys.stderr)
+        return 2
+
+    import torch
+    import exact_attention_15_amd as ea
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    dev = torch.device("cuda", 0)
+    ea.library()
+    cfg_ids = [int(x) for x in args.configs.split(",") if x]
+
+    results = {}
+    headline = None
+    for cid in cfg_ids:
+        if cid == 5:
+            continue
+        print(f"[bench] config {cid}: generating inputs", file=sys.stderr, flush=True)
+        w = fwd_workload(cid, dev)
+        r = bench_fwd(ea, w, args.steps, args.warmup)
+        c = w["cfg"]
+        results[c["name"]] = {
+            "ms_step": round(r["ms_step"], 4), "ms_kernel": round(r["ms_kernel"], 4),
+            "ms_mask_build": round(r["ms_mask_build"], 4),
+            "kernel_median_ms": round(r["dist"]["median_ms"], 4),
+            "kernel_min_ms": round(r["dist"]["min_ms"], 4),
+            "kernel_p90_ms": round(r["dist"]["p90_ms"], 4),
+            "tflops_step": round(r["tflops_step"], 2),
+            "tflops_kernel": round(r["tflops_kernel"], 2),
+            "frac_mfma_peak": round(r["tflops_kernel"] / MFMA_BF16_PEAK_TFLOPS, 4),
+            "flops": w["flops"], "visible_pairs_per_head": w["pairs_per_head"],
+        }
+        print(f"[bench] config {cid} {c['name']}: {r['ms_kernel']:.3f} ms kernel, "
+              f"{r['tflops_kernel']:.1f} TFLOP/s", file=sys.stderr, flush=True)
+        if cid == 2:
+            headline = (w, r)
+        else:
+            del w
+        torch.cuda.empty_cache()
+
+    decode_res = None
+    if 5 in cfg_ids:
+        print("[bench] config 5: generating inputs", file=sys.stderr, flush=True)
+        wd = decode_workload(dev)
+        r = bench_decode(ea, wd, args.steps, args.warmup)
+        c = wd["cfg"]
+        decode_res = {
+            "workload": c["name"], "ms": round(r["ms"], 4),
+            "median_ms": round(r["dist"]["median_ms"], 4), "min_ms": round(r["dist"]["min_ms"], 4),
+            "p90_ms": round(r["dist"]["p90_ms"], 4),
+            "algorithmic_bytes": wd["bytes"], "gbs": round(r["gbs"], 1),
+            "roofline": {"bound": "hbm", "achieved": round(r["gbs"], 1), "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": round(r["gbs"] / HBM_PEAK_GBS, 4),
+                         "traffic": None},
+        }
+        results[c["name"]] = {"ms": decode_res["ms"], "gbs": decode_res["gbs"],
+                              "frac_hbm_peak": decode_res["roofline"]["frac"]}
+        print(f"[bench] config 5: {r['ms']:.3f} ms, {r['gbs']:.0f} GB/s", file=sys.stderr, flush=True)
+        del wd
+        torch.cuda.empty_cache()
+
+    out = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+           "data": "synthetic: seeded N(0,1) bf16 inputs (x0.5 for the headline workload)"}
+    if headline is not None:
+        w, r = headline
+        c = w["cfg"]
+        out.update({
+            "value": round(r["tflops_step"], 2), "unit": "TFLOP/s",
+            "ms_per_step": round(r["ms_step"], 4),
+            "config": {"workload": c["name"], "B": c["B"], "Hq": c["Hq"], "Hkv": c["Hkv"],
+                       "N": c["N"], "d": c["d"], "mask": "causal", "scale": w["scale"],
+                       "flops_per_step": w["flops"],
+                       "step": "attn_fwd building its block mask, then the forward kernel"},
+            "roofline": {"bound": "mfma", "achieved": round(r["tflops_kernel"], 2),
+                         "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(r["tflops_kernel"] / MFMA_BF16_PEAK_TFLOPS, 4),
+                         "traffic": None,
+                         "kernel": "k_attn_fwd<128,false>",
+                         "kernel_ms": round(r["ms_kernel"], 4)},
+        })
+        if not args.no_cpu_baseline:
+            print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
+            out["cpu_baseline"] = cpu_baseline(w)
+    if decode_res is not None:
+        out["decode"] = decode_res
+    out["configs"] = results
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,254 @@
+"""ctypes binding of libexattn (argument marshalling only).
+
+Every step of the computation runs in the HIP kernels behind the C ABI in
+``include/exattn.h``.  PyTorch only supplies device memory (tensors, the
+workspace) and the stream the calls are enqueued on.  If the library is
+missing it is built in-tree; if it cannot be built or loaded, import fails --
+there is no fallback implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libexattn.so")
+
+ATTN_OK, ATTN_ERR_INVALID, ATTN_ERR_UNSUPPORTED, ATTN_ERR_WORKSPACE, ATTN_ERR_HIP = range(5)
+ATTN_MASK_CAUSAL = 1
+ATTN_MASK_WINDOW = 2
+ATTN_MASK_DOCS = 4
+ATTN_MOD_SOFTCAP = 8
+ATTN_MASK_NO_SKIP = 16
+
+# Tile sizes of the forward kernel (block-mask granularity).
+BLOCK_M = 128
+BLOCK_N = 64
+
+
+class AttnTensor(ctypes.Structure):
+    _fields_ = [("ptr", ctypes.c_void_p), ("stride_b", ctypes.c_int64),
+                ("stride_h", ctypes.c_int64), ("stride_n", ctypes.c_int64)]
+
+
+class AttnMaskSpec(ctypes.Structure):
+    _fields_ = [("flags", ctypes.c_uint32), ("window_left", ctypes.c_int32),
+                ("window_right", ctypes.c_int32), ("softcap", ctypes.c_float),
+                ("doc_offsets", ctypes.c_void_p), ("doc_stride", ctypes.c_int32)]
+
+
+class AttnError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(message)
+        self.status = status
+
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        from . import build as _build
+        _build.build()
+    lib = ctypes.CDLL(LIB_PATH)
+    P, i32, f32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    T = AttnTensor
+    SP = ctypes.POINTER(AttnMaskSpec)
+    lib.attn_mask_bytes.restype = sz
+    lib.attn_mask_bytes.argtypes = [SP, i32, i32]
+    lib.attn_mask_build.restype = i32
+    lib.attn_mask_build.argtypes = [SP, i32, i32, P, sz, P]
+    lib.attn_fwd_workspace_size.restype = sz
+    lib.attn_fwd_workspace_size.argtypes = [SP, i32, i32]
+    lib.attn_fwd.restype = i32
+    lib.attn_fwd.argtypes = [T, T, T, T, P, i32, i32, i32, i32, i32, SP, f32, P, P, sz, P]
+    lib.attn_decode_workspace_size.restype = sz
+    lib.attn_decode_workspace_size.argtypes = [i32, i32, i32, i32, i32]
+    lib.attn_decode.restype = i32
+    lib.attn_decode.argtypes = [T, T, T, P, T, P, i32, i32, i32, i32, i32, i32, f32, P, sz, P]
+    lib.attn_status_string.restype = ctypes.c_char_p
+    lib.attn_status_string.argtypes = [i32]
+    lib.attn_last_error.restype = ctypes.c_char_p
+    lib.attn_last_error.argtypes = []
+    _lib = lib
+    return lib
+
+
+def library():
+    """The loaded ctypes library (built on first use if absent)."""
+    return _load()
+
+
+def _check(status: int):
+    if status != ATTN_OK:
+        lib = _load()
+        msg = lib.attn_last_error().decode() or lib.attn_status_string(status).decode()
+        raise AttnError(status, msg)
+
+
+def _tensor4(t: torch.Tensor) -> AttnTensor:
+    if t.dim() != 4:
+        raise ValueError("expected a 4-D tensor [B, H, N, d]")
+    return AttnTensor(t.data_ptr(), t.stride(0), t.stride(1), t.stride(2))
+
+
+def _check_bf16(name, t):
+    if not t.is_cuda or t.dtype != torch.bfloat16:
+        raise TypeError(f"{name}: expected a bf16 tensor on a GPU")
+    if t.stride(-1) != 1:
+        raise ValueError(f"{name}: the head dimension must be contiguous")
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+class MaskSpec:
+    """Python holder of an ``attn_mask_spec`` (keeps doc_offsets alive)."""
+
+    def __init__(self, *, causal=False, window=None, doc_offsets=None,
+                 softcap=None, no_skip=False):
+        flags = 0
+        wl = wr = 0
+        if causal:
+            flags |= ATTN_MASK_CAUSAL
+        if window is not None:
+            flags |= ATTN_MASK_WINDOW
+            wl, wr = (window, window) if isinstance(window, int) else window
+        self.doc_offsets = None
+        doc_ptr, doc_stride = None, 0
+        if doc_offsets is not None:
+            flags |= ATTN_MASK_DOCS
+            if doc_offsets.dtype != torch.int32 or not doc_offsets.is_cuda or doc_offsets.dim() != 2:
+                raise TypeError("doc_offsets: expected an int32 [B, max_docs+1] GPU tensor")
+            self.doc_offsets = doc_offsets.contiguous()
+            doc_ptr, doc_stride = self.doc_offsets.data_ptr(), self.doc_offsets.shape[1]
+        cap = 0.0
+        if softcap is not None:
+            flags |= ATTN_MOD_SOFTCAP
+            cap = float(softcap)
+        if no_skip:
+            flags |= ATTN_MASK_NO_SKIP
+        self.c = AttnMaskSpec(flags, int(wl), int(wr), cap, doc_ptr, doc_stride)
+
+    def ref(self):
+        return ctypes.byref(self.c)
+
+
+def mask_build(spec: MaskSpec, B: int, N: int, device=None) -> torch.Tensor:
+    """Build a reusable block mask (a uint8 device buffer)."""
+    lib = _load()
+    device = device or torch.device("cuda", torch.cuda.current_device())
+    nbytes = lib.attn_mask_bytes(spec.ref(), B, N)
+    buf = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
+    _check(lib.attn_mask_build(spec.ref(), B, N, buf.data_ptr(), nbytes, _stream(device)))
+    return buf
+
+
+def fwd(q, k, v, *, causal=False, window=None, doc_offsets=None, softcap=None,
+        scale=None, block_mask=None, no_skip=False, spec=None, out=None, lse=None):
+    """Exact attention forward.  q [B,Hq,N,d], k/v [B,Hkv,N,d] bf16 (any
+    batch/head/token strides).  Returns (O [B,Hq,N,d] bf16, LSE [B,Hq,N] fp32)."""
+    lib = _load()
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check_bf16(name, t)
+    B, Hq, N, d = q.shape
+    Hkv = k.shape[1]
+    if k.shape != (B, Hkv, N, d) or v.shape != (B, Hkv, N, d):
+        raise ValueError(f"k/v must be [B, Hkv, N, d]; got {tuple(k.shape)} and {tuple(v.shape)}")
+    if spec is None:
+        spec = MaskSpec(causal=causal, window=window, doc_offsets=doc_offsets,
+                        softcap=softcap, no_skip=no_skip)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty((B, Hq, N, d), dtype=torch.bfloat16, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device)
+    ws = None
+    ws_bytes = 0
+    if block_mask is None:
+        ws_bytes = lib.attn_fwd_workspace_size(spec.ref(), B, N)
+        ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=q.device)
+    st = lib.attn_fwd(_tensor4(q), _tensor4(k), _tensor4(v), _tensor4(out), lse.data_ptr(),
+                      B, Hq, Hkv, N, d, spec.ref(), float(scale),
+                      None if block_mask is None else block_mask.data_ptr(),
+                      None if ws is None else ws.data_ptr(), ws_bytes, _stream(q.device))
+    _check(st)
+    return out, lse
+
+
+def decode(q, k_cache, v_cache, lens, *, scale=None, chunk=1024, out=None, lse=None,
+           workspace=None):
+    """Split-KV decode.  q [B,Hq,d] (or [B,Hq,1,d]), caches [B,Hkv,T,d] bf16,
+    lens int32 [B] on the GPU.  Returns (O [B,Hq,d] bf16, LSE [B,Hq] fp32)."""
+    lib = _load()
+    for name, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache)):
+        _check_bf16(name, t)
+    q4 = q if q.dim() == 4 else q.unsqueeze(2)
+    B, Hq, _, d = q4.shape
+    Hkv, T = k_cache.shape[1], k_cache.shape[2]
+    if lens.dtype != torch.int32 or not lens.is_cuda or lens.numel() != B:
+        raise TypeError("lens: expected int32 [B] on the GPU")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty((B, Hq, d), dtype=torch.bfloat16, device=q.device)
+    o4 = out if out.dim() == 4 else out.unsqueeze(2)
+    if lse is None:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    ws_bytes = lib.attn_decode_workspace_size(B, Hq, T, d, chunk)
+    if workspace is None or workspace.numel() < ws_bytes:
+        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=q.device)
+    st = lib.attn_decode(_tensor4(q4), _tensor4(k_cache), _tensor4(v_cache),
+                         lens.data_ptr(), _tensor4(o4), lse.data_ptr(), B, Hq, Hkv, T, d,
+                         int(chunk), float(scale), workspace.data_ptr(), ws_bytes,
+                         _stream(q.device))
+    _check(st)
+    return out, lse
+
+
+def decode_workspace_bytes(B, Hq, T, d, chunk=1024) -> int:
+    return _load().attn_decode_workspace_size(B, Hq, T, d, chunk)
+
+
+def mask_layout(B: int, N: int) -> dict:
+    """Offsets (bytes) of the block-mask sections, mirroring the C layout."""
+    def a256(x):
+        return (x + 255) & ~255
+    nqt = (N + BLOCK_M - 1) // BLOCK_M
+    nkt = (N + BLOCK_N - 1) // BLOCK_N
+    rows, items = B * N, B * nqt
+    off = 0
+    lay = {"nqt": nqt, "nkt": nkt}
+    lay["lo"] = off; off = a256(off + 4 * rows)
+    lay["hi"] = off; off = a256(off + 4 * rows)
+    lay["count"] = off; off = a256(off + 4 * items)
+    lay["list"] = off; off = a256(off + 4 * items * nkt)
+    lay["order"] = off; off = a256(off + 4 * items)
+    lay["bytes"] = off
+    return lay
+
+
+def mask_unpack(buf: torch.Tensor, B: int, N: int) -> dict:
+    """Host copy of a block mask's sections (for inspection and tests)."""
+    lay = mask_layout(B, N)
+    raw = buf.cpu()
+
+    def sect(name, n):
+        return raw[lay[name]: lay[name] + 4 * n].view(torch.int32).clone()
+    nqt, nkt = lay["nqt"], lay["nkt"]
+    return {
+        "lo": sect("lo", B * N).view(B, N),
+        "hi": sect("hi", B * N).view(B, N),
+        "count": sect("count", B * nqt).view(B, nqt),
+        "list": sect("list", B * nqt * nkt).view(B, nqt, nkt),
+        "order": sect("order", B * nqt),
+        "nqt": nqt, "nkt": nkt,
+    }

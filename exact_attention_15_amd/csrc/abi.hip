@@ -1,0 +1,216 @@
+// C ABI of libexattn: validation, buffer sizing and kernel launches.
+// Every check runs before any launch; the library never allocates or
+// synchronises.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "common.h"
+
+using namespace exattn;
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+attn_status fail(attn_status s, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
+attn_status fail(attn_status s, const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
+    va_end(ap);
+    return s;
+}
+
+attn_status hip_fail(hipError_t e, const char *what) {
+    return fail(ATTN_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+attn_status check_tensor(const attn_tensor &t, const char *name, bool need_n_stride) {
+    if (!t.ptr) return fail(ATTN_ERR_INVALID, "%s: null pointer", name);
+    if (!aligned16(t.ptr)) return fail(ATTN_ERR_INVALID, "%s: pointer not 16-byte aligned", name);
+    if (t.stride_b < 0 || t.stride_h < 0 || t.stride_n < 0)
+        return fail(ATTN_ERR_INVALID, "%s: negative stride", name);
+    if (t.stride_b % 8 || t.stride_h % 8 || (need_n_stride && t.stride_n % 8))
+        return fail(ATTN_ERR_INVALID, "%s: strides must be multiples of 8 elements", name);
+    return ATTN_OK;
+}
+
+const uint32_t KNOWN_FLAGS =
+    ATTN_MASK_CAUSAL | ATTN_MASK_WINDOW | ATTN_MASK_DOCS | ATTN_MOD_SOFTCAP | ATTN_MASK_NO_SKIP;
+
+attn_status check_spec(const attn_mask_spec *spec) {
+    if (!spec) return ATTN_OK;
+    if (spec->flags & ~KNOWN_FLAGS) return fail(ATTN_ERR_INVALID, "mask spec: unknown flag bits 0x%x", spec->flags);
+    if (spec->flags & ATTN_MASK_DOCS) {
+        if (!spec->doc_offsets) return fail(ATTN_ERR_INVALID, "mask spec: ATTN_MASK_DOCS needs doc_offsets");
+        if (spec->doc_stride < 2) return fail(ATTN_ERR_INVALID, "mask spec: doc_stride must be >= 2");
+    }
+    if (spec->flags & ATTN_MOD_SOFTCAP) {
+        if (!(spec->softcap > 0.f) || !std::isfinite(spec->softcap))
+            return fail(ATTN_ERR_INVALID, "mask spec: softcap must be finite and > 0");
+    }
+    return ATTN_OK;
+}
+
+attn_mask_spec spec_or_default(const attn_mask_spec *spec) {
+    attn_mask_spec s;
+    std::memset(&s, 0, sizeof s);
+    if (spec) s = *spec;
+    return s;
+}
+
+} // namespace
+
+extern "C" {
+
+const char *attn_status_string(attn_status s) {
+    switch (s) {
+    case ATTN_OK: return "ok";
+    case ATTN_ERR_INVALID: return "invalid argument";
+    case ATTN_ERR_UNSUPPORTED: return "unsupported configuration";
+    case ATTN_ERR_WORKSPACE: return "workspace too small";
+    case ATTN_ERR_HIP: return "HIP launch failure";
+    }
+    return "unknown status";
+}
+
+const char *attn_last_error(void) { return g_last_error; }
+
+size_t attn_mask_bytes(const attn_mask_spec *spec, int B, int N) {
+    (void)spec;
+    if (B <= 0 || N <= 0) return 0;
+    return mask_layout(B, N).bytes;
+}
+
+attn_status attn_mask_build(const attn_mask_spec *spec, int B, int N, void *out, size_t bytes,
+                            void *stream) {
+    if (B < 0 || N < 0) return fail(ATTN_ERR_INVALID, "attn_mask_build: B=%d N=%d", B, N);
+    attn_status st = check_spec(spec);
+    if (st != ATTN_OK) return st;
+    if (int64_t(B) * N == 0) return ATTN_OK;
+    if (!out) return fail(ATTN_ERR_INVALID, "attn_mask_build: null output buffer");
+    if (!aligned16(out)) return fail(ATTN_ERR_INVALID, "attn_mask_build: buffer not 16-byte aligned");
+    const MaskLayout L = mask_layout(B, N);
+    if (bytes < L.bytes)
+        return fail(ATTN_ERR_WORKSPACE, "attn_mask_build: need %zu bytes, got %zu", L.bytes, bytes);
+    hipError_t e = launch_mask_build(spec_or_default(spec), L, out, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "attn_mask_build");
+    return ATTN_OK;
+}
+
+size_t attn_fwd_workspace_size(const attn_mask_spec *spec, int B, int N) {
+    return attn_mask_bytes(spec, B, N);
+}
+
+attn_status attn_fwd(attn_tensor q, attn_tensor k, attn_tensor v, attn_tensor o, float *lse, int B,
+                     int Hq, int Hkv, int N, int d, const attn_mask_spec *spec, float scale,
+                     const void *block_mask, void *workspace, size_t ws_bytes, void *stream) {
+    if (B < 0 || N < 0) return fail(ATTN_ERR_INVALID, "attn_fwd: B=%d N=%d", B, N);
+    if (Hq <= 0 || Hkv <= 0) return fail(ATTN_ERR_INVALID, "attn_fwd: Hq=%d Hkv=%d", Hq, Hkv);
+    if (Hq % Hkv) return fail(ATTN_ERR_INVALID, "attn_fwd: Hq=%d is not a multiple of Hkv=%d", Hq, Hkv);
+    if (d != 64 && d != 128) return fail(ATTN_ERR_UNSUPPORTED, "attn_fwd: head dim %d (supported: 64, 128)", d);
+    if (!std::isfinite(scale) || !(scale > 0.f)) return fail(ATTN_ERR_INVALID, "attn_fwd: scale must be finite and > 0");
+    attn_status st = check_spec(spec);
+    if (st != ATTN_OK) return st;
+    if (int64_t(B) * N == 0) return ATTN_OK;
+    if ((st = check_tensor(q, "q", true)) != ATTN_OK) return st;
+    if ((st = check_tensor(k, "k", true)) != ATTN_OK) return st;
+    if ((st = check_tensor(v, "v", true)) != ATTN_OK) return st;
+    if ((st = check_tensor(o, "o", true)) != ATTN_OK) return st;
+    if (!lse) return fail(ATTN_ERR_INVALID, "attn_fwd: null lse");
+    const MaskLayout L = mask_layout(B, N);
+    if (int64_t(B) * L.nqt * Hq > 0x7FFFFFFFLL) return fail(ATTN_ERR_UNSUPPORTED, "attn_fwd: grid too large");
+    const attn_mask_spec sp = spec_or_default(spec);
+    const void *mask = block_mask;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (!mask) {
+        if (!workspace || ws_bytes < L.bytes)
+            return fail(ATTN_ERR_WORKSPACE, "attn_fwd: workspace needs %zu bytes, got %zu", L.bytes,
+                        workspace ? ws_bytes : size_t(0));
+        if (!aligned16(workspace)) return fail(ATTN_ERR_INVALID, "attn_fwd: workspace not 16-byte aligned");
+        hipError_t e = launch_mask_build(sp, L, workspace, s);
+        if (e != hipSuccess) return hip_fail(e, "attn_fwd (mask build)");
+        mask = workspace;
+    }
+    FwdParams p;
+    p.q = static_cast<const uint16_t *>(q.ptr);
+    p.k = static_cast<const uint16_t *>(k.ptr);
+    p.v = static_cast<const uint16_t *>(v.ptr);
+    p.o = static_cast<uint16_t *>(o.ptr);
+    p.lse = lse;
+    p.q_sb = q.stride_b; p.q_sh = q.stride_h; p.q_sn = q.stride_n;
+    p.k_sb = k.stride_b; p.k_sh = k.stride_h; p.k_sn = k.stride_n;
+    p.v_sb = v.stride_b; p.v_sh = v.stride_h; p.v_sn = v.stride_n;
+    p.o_sb = o.stride_b; p.o_sh = o.stride_h; p.o_sn = o.stride_n;
+    p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.N = N; p.nqt = L.nqt; p.nkt = L.nkt;
+    const float log2e = 1.4426950408889634f;
+    p.scale_log2 = scale * log2e;
+    const bool softcap = sp.flags & ATTN_MOD_SOFTCAP;
+    p.softcap = softcap ? sp.softcap : 0.f;
+    p.cap_inv_scale = softcap ? scale / sp.softcap : 0.f;
+    p.cap_log2 = softcap ? sp.softcap * log2e : 0.f;
+    p.mask = mask_view(mask, L);
+    hipError_t e = launch_fwd(p, d, softcap, s);
+    if (e != hipSuccess) return hip_fail(e, "attn_fwd");
+    return ATTN_OK;
+}
+
+size_t attn_decode_workspace_size(int B, int Hq, int T, int d, int chunk) {
+    if (B <= 0 || Hq <= 0 || T < 0 || d <= 0 || chunk <= 0) return 0;
+    const int nchunk = T > 0 ? (T + chunk - 1) / chunk : 1;
+    return decode_ws_bytes(B, Hq, nchunk, d, nullptr, nullptr);
+}
+
+attn_status attn_decode(attn_tensor q, attn_tensor k_cache, attn_tensor v_cache, const int32_t *lens,
+                        attn_tensor o, float *lse, int B, int Hq, int Hkv, int T, int d, int chunk,
+                        float scale, void *workspace, size_t ws_bytes, void *stream) {
+    if (B < 0 || T < 0) return fail(ATTN_ERR_INVALID, "attn_decode: B=%d T=%d", B, T);
+    if (Hq <= 0 || Hkv <= 0) return fail(ATTN_ERR_INVALID, "attn_decode: Hq=%d Hkv=%d", Hq, Hkv);
+    if (Hq % Hkv) return fail(ATTN_ERR_INVALID, "attn_decode: Hq=%d is not a multiple of Hkv=%d", Hq, Hkv);
+    if (Hq / Hkv > 16) return fail(ATTN_ERR_UNSUPPORTED, "attn_decode: group size %d > 16", Hq / Hkv);
+    if (d != 64 && d != 128) return fail(ATTN_ERR_UNSUPPORTED, "attn_decode: head dim %d (supported: 64, 128)", d);
+    if (chunk < 64 || chunk > 2048 || chunk % 64)
+        return fail(ATTN_ERR_UNSUPPORTED, "attn_decode: chunk %d (multiple of 64 in [64, 2048])", chunk);
+    if (!std::isfinite(scale) || !(scale > 0.f)) return fail(ATTN_ERR_INVALID, "attn_decode: scale must be finite and > 0");
+    if (B == 0) return ATTN_OK;
+    attn_status st;
+    if ((st = check_tensor(q, "q", false)) != ATTN_OK) return st;
+    if ((st = check_tensor(k_cache, "k_cache", true)) != ATTN_OK) return st;
+    if ((st = check_tensor(v_cache, "v_cache", true)) != ATTN_OK) return st;
+    if ((st = check_tensor(o, "o", false)) != ATTN_OK) return st;
+    if (!lens) return fail(ATTN_ERR_INVALID, "attn_decode: null lens");
+    if (!lse) return fail(ATTN_ERR_INVALID, "attn_decode: null lse");
+    const int nchunk = T > 0 ? (T + chunk - 1) / chunk : 1;
+    size_t off_l = 0, off_o = 0;
+    const size_t need = decode_ws_bytes(B, Hq, nchunk, d, &off_l, &off_o);
+    if (!workspace || ws_bytes < need)
+        return fail(ATTN_ERR_WORKSPACE, "attn_decode: workspace needs %zu bytes, got %zu", need,
+                    workspace ? ws_bytes : size_t(0));
+    if (!aligned16(workspace)) return fail(ATTN_ERR_INVALID, "attn_decode: workspace not 16-byte aligned");
+    DecodeParams p;
+    p.q = static_cast<const uint16_t *>(q.ptr);
+    p.k = static_cast<const uint16_t *>(k_cache.ptr);
+    p.v = static_cast<const uint16_t *>(v_cache.ptr);
+    p.o = static_cast<uint16_t *>(o.ptr);
+    p.lse = lse;
+    p.lens = lens;
+    p.q_sb = q.stride_b; p.q_sh = q.stride_h;
+    p.k_sb = k_cache.stride_b; p.k_sh = k_cache.stride_h; p.k_sn = k_cache.stride_n;
+    p.v_sb = v_cache.stride_b; p.v_sh = v_cache.stride_h; p.v_sn = v_cache.stride_n;
+    p.o_sb = o.stride_b; p.o_sh = o.stride_h;
+    p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.T = T; p.chunk = chunk; p.nchunk = nchunk;
+    p.scale_log2 = scale * 1.4426950408889634f;
+    char *ws = static_cast<char *>(workspace);
+    p.part_m = reinterpret_cast<float *>(ws);
+    p.part_l = reinterpret_cast<float *>(ws + off_l);
+    p.part_o = reinterpret_cast<float *>(ws + off_o);
+    hipError_t e = launch_decode(p, d, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "attn_decode");
+    return ATTN_OK;
+}
+
+} // extern "C"

@@ -1,0 +1,110 @@
+// Internal declarations shared by the HIP translation units of libexattn.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/exattn.h"
+
+namespace exattn {
+
+// Forward tiling: a workgroup owns BLOCK_M query rows (4 waves x 32 rows)
+// and sweeps key tiles of BLOCK_N keys.
+constexpr int BLOCK_M = 128;
+constexpr int BLOCK_N = 64;
+
+// Block-mask entry: (key tile index << 1) | partial-bit.
+constexpr int32_t TILE_PARTIAL = 1;
+
+// Device layout of a block mask (all int32, each section 256-byte aligned).
+struct MaskLayout {
+    int B, N, nqt, nkt;
+    size_t off_lo, off_hi, off_count, off_list, off_order, bytes;
+};
+
+inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+inline MaskLayout mask_layout(int B, int N) {
+    MaskLayout L;
+    L.B = B;
+    L.N = N;
+    L.nqt = (N + BLOCK_M - 1) / BLOCK_M;
+    L.nkt = (N + BLOCK_N - 1) / BLOCK_N;
+    size_t rows = size_t(B) * size_t(N);
+    size_t items = size_t(B) * size_t(L.nqt);
+    size_t off = 0;
+    L.off_lo = off;    off = align256(off + 4 * rows);
+    L.off_hi = off;    off = align256(off + 4 * rows);
+    L.off_count = off; off = align256(off + 4 * items);
+    L.off_list = off;  off = align256(off + 4 * items * size_t(L.nkt));
+    L.off_order = off; off = align256(off + 4 * items);
+    L.bytes = off;
+    return L;
+}
+
+struct MaskView {
+    const int32_t *lo, *hi, *count, *list, *order;
+};
+
+inline MaskView mask_view(const void *base, const MaskLayout &L) {
+    const char *p = static_cast<const char *>(base);
+    MaskView v;
+    v.lo = reinterpret_cast<const int32_t *>(p + L.off_lo);
+    v.hi = reinterpret_cast<const int32_t *>(p + L.off_hi);
+    v.count = reinterpret_cast<const int32_t *>(p + L.off_count);
+    v.list = reinterpret_cast<const int32_t *>(p + L.off_list);
+    v.order = reinterpret_cast<const int32_t *>(p + L.off_order);
+    return v;
+}
+
+// Launchers (each returns hipSuccess or the launch error).
+hipError_t launch_mask_build(const attn_mask_spec &spec, const MaskLayout &L,
+                             void *out, hipStream_t stream);
+
+struct FwdParams {
+    const uint16_t *q, *k, *v;
+    uint16_t *o;
+    float *lse;
+    int64_t q_sb, q_sh, q_sn;
+    int64_t k_sb, k_sh, k_sn;
+    int64_t v_sb, v_sh, v_sn;
+    int64_t o_sb, o_sh, o_sn;
+    int B, Hq, Hkv, N, nqt, nkt;
+    float scale_log2;    // scale * log2(e): scores in base-2 units
+    float softcap;       // cap c (softcap mode only)
+    float cap_inv_scale; // scale / c (softcap mode only)
+    float cap_log2;      // c * log2(e) (softcap mode only)
+    MaskView mask;
+};
+
+hipError_t launch_fwd(const FwdParams &p, int d, bool softcap, hipStream_t stream);
+
+struct DecodeParams {
+    const uint16_t *q, *k, *v;
+    uint16_t *o;
+    float *lse;
+    const int32_t *lens;
+    int64_t q_sb, q_sh;
+    int64_t k_sb, k_sh, k_sn;
+    int64_t v_sb, v_sh, v_sn;
+    int64_t o_sb, o_sh;
+    int B, Hq, Hkv, T, chunk, nchunk;
+    float scale_log2;
+    float *part_m, *part_l, *part_o; // workspace partials
+};
+
+hipError_t launch_decode(const DecodeParams &p, int d, hipStream_t stream);
+
+// Workspace layout of attn_decode: m, l [B][Hq][nchunk], O [B][Hq][nchunk][d].
+inline size_t decode_ws_bytes(int B, int Hq, int nchunk, int d, size_t *off_l,
+                              size_t *off_o) {
+    size_t n = size_t(B) * size_t(Hq) * size_t(nchunk);
+    size_t off = align256(4 * n);
+    if (off_l) *off_l = off;
+    off = align256(off + 4 * n);
+    if (off_o) *off_o = off;
+    off = align256(off + 4 * n * size_t(d));
+    return off;
+}
+
+} // namespace exattn

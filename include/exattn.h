@@ -1,0 +1,167 @@
+/*
+ * exattn.h -- C ABI of the MI355X (gfx950) exact-attention library.
+ *
+ * The library computes exact softmax(Q K^T * scale) V tile by tile with an
+ * online softmax (running row max m and running sum l, rescaling the output
+ * block by block), so the N x N score and probability matrices never reach
+ * HBM.  Sources for the operation:
+ *   - the attention definition and its tiling/online-softmax form:
+ *     youngju.dev "FlashAttention 논문 분석: IO-Aware Exact Attention...",
+ *     sections "수학적 정의", "Online Softmax와 블록 단위 누적" and
+ *     "알고리즘 의사코드";
+ *   - register-level score modifications and masks (causal, sliding window,
+ *     document boundaries) and block-level skipping of fully masked tiles:
+ *     it-trends-board "PyTorch FlexAttention 도입 분석", section 2;
+ *   - GQA, soft cap, packed documents and split-KV decode with a combine:
+ *     aegloslab "3.7 어텐션 II — 융합 커널·실전 라이브러리", sections 3.7.4
+ *     to 3.7.6.
+ *
+ * Conventions shared by every entry point
+ *   - Device pointers are HIP device memory owned by the caller.  The library
+ *     never allocates, frees or synchronises; it enqueues work on `stream`
+ *     (a hipStream_t passed as void*, NULL = the default stream) and returns.
+ *     Buffers must stay valid until that work completes.
+ *   - Tensors are bf16 (stored as raw 16-bit values) with a unit stride on
+ *     the head dimension d and explicit element strides for batch, head and
+ *     token, so [B,H,N,d] and [B,N,H,d] layouts both work without copies.
+ *     Pointers must be 16-byte aligned and strides multiples of 8 elements.
+ *   - A non-OK status means nothing was enqueued, except ATTN_ERR_HIP (a
+ *     launch failed after validation).  attn_last_error() gives a message
+ *     for the calling thread's last non-OK status.  There is no fallback
+ *     path: unsupported input is an error.
+ *   - Calls on one stream are ordered; calls that share a workspace or block
+ *     mask buffer on different streams race.
+ */
+#ifndef EXATTN_H
+#define EXATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    ATTN_OK = 0,
+    ATTN_ERR_INVALID = 1,     /* malformed argument (null pointer, bad size, misaligned) */
+    ATTN_ERR_UNSUPPORTED = 2, /* well-formed but not implemented (head dim, group size) */
+    ATTN_ERR_WORKSPACE = 3,   /* workspace / block-mask buffer too small */
+    ATTN_ERR_HIP = 4          /* a kernel launch failed */
+} attn_status;
+
+/* Mask and score-modification flags (attn_mask_spec.flags), combined by AND. */
+enum {
+    ATTN_MASK_CAUSAL = 1u,  /* key j visible to query i only if j <= i */
+    ATTN_MASK_WINDOW = 2u,  /* visible only if i - window_left <= j <= i + window_right */
+    ATTN_MASK_DOCS = 4u,    /* visible only inside the query's document */
+    ATTN_MOD_SOFTCAP = 8u,  /* visible scores s -> softcap * tanh(s / softcap) */
+    ATTN_MASK_NO_SKIP = 16u /* diagnostic: visit every key tile (none skipped,
+                               all element-masked); results are bitwise equal */
+};
+
+/*
+ * Mask specification.  Every supported mask gives each query row one
+ * contiguous interval of visible keys, which is what the block mask stores.
+ * The scaled score is masked to -inf first; the soft cap then applies to the
+ * remaining scores only, so masked keys get weight exactly 0.
+ */
+typedef struct {
+    uint32_t flags;
+    int32_t window_left;        /* ATTN_MASK_WINDOW: keys before i that stay visible */
+    int32_t window_right;       /* ATTN_MASK_WINDOW: keys after i that stay visible */
+    float softcap;              /* ATTN_MOD_SOFTCAP: cap c > 0 */
+    const int32_t *doc_offsets; /* ATTN_MASK_DOCS: device int32 [B][doc_stride], per
+                                   row 0 = o_0 < o_1 < ... < o_n = N, padded with N
+                                   (cumulative document boundaries) */
+    int32_t doc_stride;         /* entries per batch row (max documents + 1), >= 2 */
+} attn_mask_spec;
+
+/* A strided bf16 tensor view: element (b, h, n, t) lives at
+ * ptr + b*stride_b + h*stride_h + n*stride_n + t (in 2-byte elements). */
+typedef struct {
+    void *ptr;
+    int64_t stride_b, stride_h, stride_n;
+} attn_tensor;
+
+/*
+ * Block mask: per-row visible key intervals, and for every 128-query tile
+ * the list of 64-key tiles that hold at least one visible key, each marked
+ * FULL (no element mask needed) or PARTIAL, plus a heavy-first order of the
+ * query tiles.  Fully masked tiles are never visited (it-trends-board
+ * "PyTorch FlexAttention 도입 분석", section 2, the block-mask early-out;
+ * youngju.dev "FlashAttention 논문 분석", FlashAttention-2 improvement 1:
+ * blocks that need no mask skip the masking).
+ *
+ * attn_mask_bytes: size in bytes of the block mask for (spec, B, N).
+ * attn_mask_build: builds it into `out` (device memory, >= attn_mask_bytes)
+ *   on `stream`.  Depends only on the spec, B and N (never on heads or data),
+ *   so one build serves any number of attn_fwd calls with the same mask.
+ *   Errors: ATTN_ERR_INVALID (null spec/out with B*N > 0, B < 0, N < 0, bad
+ *   doc_stride, softcap <= 0 with ATTN_MOD_SOFTCAP), ATTN_ERR_WORKSPACE
+ *   (bytes too small), ATTN_ERR_HIP.
+ */
+size_t attn_mask_bytes(const attn_mask_spec *spec, int B, int N);
+attn_status attn_mask_build(const attn_mask_spec *spec, int B, int N, void *out,
+                            size_t bytes, void *stream);
+
+/*
+ * Forward attention (prefill, Nq = Nk = N).
+ *   q [B,Hq,N,d], k and v [B,Hkv,N,d]: bf16 inputs; query head h reads KV
+ *     head h / (Hq/Hkv) (grouped-query attention, no K/V copies).
+ *   o [B,Hq,N,d]: bf16 output, normalised (O = P V with rows of P summing
+ *     to 1), rounded to nearest even.
+ *   lse: fp32 [B][Hq][N] contiguous, natural-log log-sum-exp of the final
+ *     (scaled, masked, capped) scores of each row; -inf (and O = 0) for a
+ *     row with no visible key.
+ *   scale: multiplies q.k before masking; finite and > 0 (1/sqrt(d) is the
+ *     usual choice).
+ *   block_mask: a buffer built by attn_mask_build with the same spec, B and
+ *     N, or NULL.  If NULL the call builds one in `workspace` first, which
+ *     then needs attn_fwd_workspace_size bytes; otherwise workspace may be
+ *     NULL with ws_bytes 0.
+ * Supported: d in {64, 128}; Hq % Hkv == 0; N >= 0; B >= 0 (B*N == 0 is a
+ * no-op).  Errors: ATTN_ERR_INVALID, ATTN_ERR_UNSUPPORTED (other d),
+ * ATTN_ERR_WORKSPACE, ATTN_ERR_HIP.
+ */
+size_t attn_fwd_workspace_size(const attn_mask_spec *spec, int B, int N);
+attn_status attn_fwd(attn_tensor q, attn_tensor k, attn_tensor v, attn_tensor o,
+                     float *lse, int B, int Hq, int Hkv, int N, int d,
+                     const attn_mask_spec *spec, float scale,
+                     const void *block_mask, void *workspace, size_t ws_bytes,
+                     void *stream);
+
+/*
+ * Split-KV decode: one new query per (batch row, query head) against the
+ * first lens[b] keys of a KV cache (aegloslab "3.7 어텐션 II", section
+ * 3.7.4).  The valid keys are cut into chunks of `chunk` keys; every
+ * (b, KV head, chunk) is processed in parallel, producing partial row max,
+ * sum and unnormalised output for the whole GQA group, and a second kernel
+ * merges the partials by rescaling each with exp(m_c - max_c m_c).
+ *   q [B,Hq,1,d] (stride_n unused), k_cache and v_cache [B,Hkv,T,d] bf16.
+ *   lens: device int32 [B], 0 <= lens[b] <= T (values outside are clamped
+ *     into [0, T]); keys at positions >= lens[b] are never read.
+ *   o [B,Hq,1,d] bf16 (stride_n unused); lse fp32 [B][Hq] contiguous
+ *     (natural log; -inf and O = 0 when lens[b] == 0).
+ *   chunk: keys per split, a multiple of 64 in [64, 2048].
+ *   workspace: >= attn_decode_workspace_size(B, Hq, T, d, chunk) bytes.
+ * Supported: d in {64, 128}; Hq % Hkv == 0 with Hq/Hkv <= 16.
+ * Errors: ATTN_ERR_INVALID, ATTN_ERR_UNSUPPORTED, ATTN_ERR_WORKSPACE,
+ * ATTN_ERR_HIP.
+ */
+size_t attn_decode_workspace_size(int B, int Hq, int T, int d, int chunk);
+attn_status attn_decode(attn_tensor q, attn_tensor k_cache, attn_tensor v_cache,
+                        const int32_t *lens, attn_tensor o, float *lse, int B,
+                        int Hq, int Hkv, int T, int d, int chunk, float scale,
+                        void *workspace, size_t ws_bytes, void *stream);
+
+/* Static description of a status code. */
+const char *attn_status_string(attn_status status);
+/* Detail for the calling thread's most recent non-OK status ("" if none). */
+const char *attn_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* EXATTN_H */

@@ -1,0 +1,115 @@
+"""Host-side checks of the C ABI (no GPU needed).
+
+The library must load, export every function that include/exattn.h
+declares, size its buffers consistently, and reject malformed calls with
+the documented status before touching the GPU (validation runs before any
+HIP call, so these calls are safe without a device).
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "exattn.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(attn_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from exact_attention_15_amd import binding
+    return binding.library()
+
+
+def test_header_declares_the_boundary():
+    names = _declared_functions()
+    for n in ("attn_fwd", "attn_decode", "attn_mask_build", "attn_mask_bytes",
+              "attn_fwd_workspace_size", "attn_decode_workspace_size",
+              "attn_status_string", "attn_last_error"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings(lib):
+    for s in range(5):
+        assert lib.attn_status_string(s)
+    assert lib.attn_status_string(99) == b"unknown status"
+
+
+def test_mask_bytes_matches_python_layout(lib):
+    from exact_attention_15_amd import binding
+    spec = binding.MaskSpec(causal=True)
+    for B, N in [(1, 1), (1, 256), (2, 1000), (8, 4096), (4, 16384)]:
+        assert lib.attn_mask_bytes(spec.ref(), B, N) == binding.mask_layout(B, N)["bytes"]
+    assert lib.attn_mask_bytes(spec.ref(), 0, 10) == 0
+
+
+def test_decode_workspace_size(lib):
+    # m and l: B*Hq*nchunk floats each; O: B*Hq*nchunk*d floats (256-byte aligned sections)
+    B, Hq, T, d, chunk = 16, 32, 32768, 128, 1024
+    n = B * Hq * (T // chunk)
+    assert lib.attn_decode_workspace_size(B, Hq, T, d, chunk) == 4 * n * 2 + 4 * n * d
+
+
+def _t(ptr=16, sb=0, sh=0, sn=0):
+    from exact_attention_15_amd.binding import AttnTensor
+    return AttnTensor(ptr, sb, sh, sn)
+
+
+def _fwd(lib, d=128, Hq=4, Hkv=2, scale=0.1, B=1, N=8, ptr=16, ws=None, ws_bytes=0):
+    t = _t(ptr, 0, 0, 128)
+    lse = ctypes.c_void_p(16)
+    return lib.attn_fwd(t, t, t, t, lse, B, Hq, Hkv, N, d, None, ctypes.c_float(scale),
+                        None, ws, ws_bytes, None)
+
+
+def test_fwd_validation_before_launch(lib):
+    from exact_attention_15_amd import binding as b
+    assert _fwd(lib, d=96) == b.ATTN_ERR_UNSUPPORTED
+    assert b"head dim 96" in lib.attn_last_error()
+    assert _fwd(lib, Hq=3, Hkv=2) == b.ATTN_ERR_INVALID
+    assert _fwd(lib, scale=0.0) == b.ATTN_ERR_INVALID
+    assert _fwd(lib, scale=float("nan")) == b.ATTN_ERR_INVALID
+    assert _fwd(lib, ptr=18) == b.ATTN_ERR_INVALID                  # misaligned
+    assert _fwd(lib, ws=None) == b.ATTN_ERR_WORKSPACE                # no block mask, no workspace
+    assert _fwd(lib, ws=ctypes.c_void_p(16), ws_bytes=8) == b.ATTN_ERR_WORKSPACE
+    assert _fwd(lib, B=0) == b.ATTN_OK                               # empty: nothing to do
+    assert _fwd(lib, N=0) == b.ATTN_OK
+
+
+def test_fwd_rejects_bad_specs(lib):
+    from exact_attention_15_amd import binding as b
+    t = _t(16, 0, 0, 128)
+    for spec in (b.AttnMaskSpec(b.ATTN_MASK_DOCS, 0, 0, 0.0, None, 2),
+                 b.AttnMaskSpec(b.ATTN_MASK_DOCS, 0, 0, 0.0, 64, 1),
+                 b.AttnMaskSpec(b.ATTN_MOD_SOFTCAP, 0, 0, 0.0, None, 0),
+                 b.AttnMaskSpec(1 << 10, 0, 0, 0.0, None, 0)):
+        st = lib.attn_fwd(t, t, t, t, ctypes.c_void_p(16), 1, 2, 2, 8, 128, ctypes.byref(spec),
+                          ctypes.c_float(0.1), None, None, 0, None)
+        assert st == b.ATTN_ERR_INVALID
+
+
+def test_decode_validation_before_launch(lib):
+    from exact_attention_15_amd import binding as b
+    t = _t(16, 0, 0, 128)
+
+    def call(Hq=8, Hkv=2, d=128, chunk=1024, ws=None, ws_bytes=0, lens=16, T=4096):
+        return lib.attn_decode(t, t, t, lens, t, ctypes.c_void_p(16), 2, Hq, Hkv, T, d, chunk,
+                               ctypes.c_float(0.1), ws, ws_bytes, None)
+    assert call(d=80) == b.ATTN_ERR_UNSUPPORTED
+    assert call(Hq=34, Hkv=2) == b.ATTN_ERR_UNSUPPORTED   # group of 17
+    assert call(Hq=6, Hkv=4) == b.ATTN_ERR_INVALID
+    assert call(chunk=1000) == b.ATTN_ERR_UNSUPPORTED
+    assert call(chunk=4096) == b.ATTN_ERR_UNSUPPORTED
+    assert call(lens=None) == b.ATTN_ERR_INVALID
+    assert call() == b.ATTN_ERR_WORKSPACE

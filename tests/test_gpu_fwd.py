@@ -1,0 +1,234 @@
+"""GPU parity of the forward path (block-mask builder + forward kernel)
+against the fp64 oracle, element by element, through the C ABI."""
+import math
+
+import numpy as np
+import pytest
+
+import attn_inputs as gen
+import oracle
+from tests.helpers import bf16_to_f64, compare, to_dev
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def ea():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import exact_attention_15_amd as ea
+    ea.library()
+    return ea
+
+
+def _docs_dev(offs_rows, N):
+    padded, _ = gen.pad_offsets(offs_rows, N)
+    return padded, torch.from_numpy(padded).cuda()
+
+
+def run_case(ea, *, B, Hq, Hkv, N, d, seed, factor=1.0, causal=False, window=None,
+             softcap=None, docs=None, scale=None, label=""):
+    q, k, v, _ = gen.fwd_inputs(seed, B, Hq, Hkv, N, d, factor)
+    scale = scale if scale is not None else 1.0 / math.sqrt(d)
+    kw_dev, kw_ref = {}, {}
+    if docs is not None:
+        padded, dev = _docs_dev(docs, N)
+        kw_dev["doc_offsets"] = dev
+        kw_ref["doc_offsets"] = padded
+    print(f"[case] {label} B={B} Hq={Hq} Hkv={Hkv} N={N} d={d} causal={causal} "
+          f"window={window} softcap={softcap} docs={docs is not None}", flush=True)
+    o, lse = ea.fwd(to_dev(q), to_dev(k), to_dev(v), causal=causal, window=window,
+                    softcap=softcap, scale=scale, **kw_dev)
+    torch.cuda.synchronize()
+    ro, rl = oracle.fwd(q, k, v, scale=scale, causal=causal, window=window,
+                        softcap=softcap, **kw_ref)
+    return compare(bf16_to_f64(o), lse.cpu().numpy(), ro, rl, label)
+
+
+def test_small_causal_config(ea):
+    # the small causal workload: B=1, H=2, N=256, d=64, scale 1/8
+    c = gen.CONFIGS[1]
+    run_case(ea, B=1, Hq=2, Hkv=2, N=256, d=64, seed=c["seed"], causal=True, label="cfg1")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("N", [1, 65, 1000])
+def test_causal_ragged(ea, d, N):
+    run_case(ea, B=2, Hq=3, Hkv=3, N=N, d=d, seed=11 + N, causal=True, factor=0.5,
+             label=f"causal N={N} d={d}")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_full_bidirectional(ea, d):
+    run_case(ea, B=1, Hq=2, Hkv=1, N=777, d=d, seed=21, label="no mask")
+
+
+def test_window_softcap(ea):
+    run_case(ea, B=1, Hq=2, Hkv=2, N=3000, d=128, seed=31, window=300, softcap=50.0,
+             label="window300+cap50")
+
+
+def test_window_1024_softcap_rows(ea):
+    run_case(ea, B=1, Hq=1, Hkv=1, N=4100, d=128, seed=32, window=1024, softcap=50.0,
+             label="window1024+cap50")
+
+
+def test_left_window_and_causal(ea):
+    run_case(ea, B=1, Hq=2, Hkv=2, N=1500, d=64, seed=33, window=(200, 0), label="left window")
+    run_case(ea, B=1, Hq=2, Hkv=2, N=1500, d=128, seed=34, window=(129, 0), causal=True,
+             label="left window+causal")
+
+
+def test_window_zero_is_identity(ea):
+    q, k, v, _ = gen.fwd_inputs(35, 1, 2, 2, 300, 128)
+    o, lse = ea.fwd(to_dev(q), to_dev(k), to_dev(v), window=0)
+    torch.cuda.synchronize()
+    assert np.array_equal(bf16_to_f64(o), gen.f32_from_bf16_bits(v).astype(np.float64))
+
+
+def test_empty_rows(ea):
+    # keys i+1..i+2 only: the last row sees nothing -> O = 0, LSE = -inf
+    run_case(ea, B=1, Hq=2, Hkv=2, N=200, d=128, seed=36, window=(-1, 2), label="future-only")
+
+
+def test_softcap_large_scores(ea):
+    # scale 1 and factor 2: scaled scores reach hundreds, so the cap (c=20) dominates
+    run_case(ea, B=1, Hq=2, Hkv=2, N=700, d=128, seed=37, factor=2.0, scale=1.0,
+             softcap=20.0, causal=True, label="cap20 scale1")
+
+
+@pytest.mark.parametrize("group", [1, 4, 8])
+def test_gqa_docs_causal(ea, group):
+    rng = np.random.Generator(np.random.PCG64(41 + group))
+    N = 2048
+    docs = gen.draw_doc_offsets(rng, 2, N, 64, 700)
+    run_case(ea, B=2, Hq=8, Hkv=8 // group, N=N, d=128, seed=42 + group, causal=True,
+             docs=docs, label=f"gqa{group} docs")
+
+
+def test_single_document_equals_causal(ea):
+    q, k, v, _ = gen.fwd_inputs(51, 2, 4, 2, 1100, 128)
+    Q, K, V = to_dev(q), to_dev(k), to_dev(v)
+    offs = torch.tensor([[0, 1100], [0, 1100]], dtype=torch.int32, device="cuda")
+    o1, l1 = ea.fwd(Q, K, V, causal=True, doc_offsets=offs)
+    o2, l2 = ea.fwd(Q, K, V, causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_docs_without_causal(ea):
+    rng = np.random.Generator(np.random.PCG64(52))
+    docs = gen.draw_doc_offsets(rng, 1, 1500, 100, 600)
+    run_case(ea, B=1, Hq=2, Hkv=2, N=1500, d=64, seed=53, docs=docs, label="docs bidirectional")
+
+
+@pytest.mark.parametrize("kind", ["causal", "window", "docs"])
+def test_block_skipping_is_bitwise_neutral(ea, kind):
+    N = 1500
+    q, k, v, _ = gen.fwd_inputs(61, 1, 4, 2, N, 128)
+    Q, K, V = to_dev(q), to_dev(k), to_dev(v)
+    kw = {}
+    if kind == "causal":
+        kw = dict(causal=True)
+    elif kind == "window":
+        kw = dict(window=200, softcap=50.0)
+    else:
+        rng = np.random.Generator(np.random.PCG64(62))
+        _, dev = _docs_dev(gen.draw_doc_offsets(rng, 1, N, 100, 500), N)
+        kw = dict(causal=True, doc_offsets=dev)
+    o1, l1 = ea.fwd(Q, K, V, **kw)
+    o2, l2 = ea.fwd(Q, K, V, no_skip=True, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2)
+    assert torch.equal(l1, l2)
+
+
+def test_strided_layout_bnhd(ea):
+    # [B, N, H, d] storage viewed as [B, H, N, d]: no copies, same result
+    q, k, v, _ = gen.fwd_inputs(71, 2, 4, 4, 600, 128)
+    Q, K, V = to_dev(q), to_dev(k), to_dev(v)
+    Qt = Q.transpose(1, 2).contiguous().transpose(1, 2)
+    Kt = K.transpose(1, 2).contiguous().transpose(1, 2)
+    Vt = V.transpose(1, 2).contiguous().transpose(1, 2)
+    assert Qt.stride(1) == 128 and not Qt.is_contiguous()
+    o1, l1 = ea.fwd(Q, K, V, causal=True)
+    out = torch.empty(2, 600, 4, 128, dtype=torch.bfloat16, device="cuda").transpose(1, 2)
+    o2, l2 = ea.fwd(Qt, Kt, Vt, causal=True, out=out)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_prebuilt_block_mask_is_reusable(ea):
+    q, k, v, _ = gen.fwd_inputs(81, 1, 2, 2, 900, 128)
+    Q, K, V = to_dev(q), to_dev(k), to_dev(v)
+    spec = ea.MaskSpec(causal=True)
+    bm = ea.mask_build(spec, 1, 900)
+    o1, l1 = ea.fwd(Q, K, V, spec=spec, block_mask=bm)
+    o2, l2 = ea.fwd(Q, K, V, causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+# --------------------------------------------------------------------------
+# Block-mask builder vs a host classification of the same intervals.
+# --------------------------------------------------------------------------
+def _host_intervals(kind, B, N, docs):
+    i = np.arange(N)
+    lo = np.zeros((B, N), np.int64)
+    hi = np.tile(np.arange(N) * 0 + N - 1, (B, 1)).astype(np.int64)
+    if kind in ("causal", "docs"):
+        hi = np.minimum(hi, i)
+    if kind == "window":
+        lo = np.maximum(lo, i - 300)
+        hi = np.minimum(hi, i + 300)
+    if kind == "docs":
+        for b in range(B):
+            offs = docs[b]
+            idx = np.searchsorted(offs, i, side="right") - 1
+            lo[b] = np.maximum(lo[b], offs[idx])
+            hi[b] = np.minimum(hi[b], offs[idx + 1] - 1)
+    return lo, hi
+
+
+@pytest.mark.parametrize("kind", ["causal", "window", "docs"])
+@pytest.mark.parametrize("N", [256, 1000, 4096])
+def test_mask_builder_matches_host(ea, kind, N):
+    B = 2
+    docs_dev = None
+    docs = None
+    if kind == "docs":
+        rng = np.random.Generator(np.random.PCG64(N))
+        docs = gen.draw_doc_offsets(rng, B, N, 64, 900)
+        _, docs_dev = _docs_dev(docs, N)
+    spec = ea.MaskSpec(causal=kind in ("causal", "docs"), window=300 if kind == "window" else None,
+                       doc_offsets=docs_dev)
+    bm = ea.mask_build(spec, B, N)
+    torch.cuda.synchronize()
+    m = ea.mask_unpack(bm, B, N)
+    lo, hi = _host_intervals(kind, B, N, docs)
+    assert np.array_equal(m["lo"].numpy(), lo) and np.array_equal(m["hi"].numpy(), hi)
+    nqt, nkt = m["nqt"], m["nkt"]
+    BM, BN = ea.BLOCK_M, ea.BLOCK_N
+    counts = np.zeros((B, nqt), np.int64)
+    for b in range(B):
+        for qt in range(nqt):
+            rows = np.arange(qt * BM, min(N, qt * BM + BM))
+            expect = []
+            for kt in range(nkt):
+                c0, c1 = kt * BN, kt * BN + BN - 1
+                any_vis = np.any(np.maximum(lo[b, rows], c0) <= np.minimum(hi[b, rows], c1))
+                full = np.all((lo[b, rows] <= c0) & (hi[b, rows] >= c1))
+                if any_vis:
+                    expect.append(kt * 2 + (0 if full else 1))
+            counts[b, qt] = len(expect)
+            got = m["list"][b, qt, : len(expect)].numpy().tolist()
+            assert m["count"][b, qt].item() == len(expect)
+            assert got == expect, (b, qt)
+    # heavy-first order: a permutation, counts non-increasing, ties by index
+    order = m["order"].numpy()
+    flat = counts.reshape(-1)
+    assert sorted(order.tolist()) == list(range(B * nqt))
+    expect_order = sorted(range(B * nqt), key=lambda x: (-flat[x], x))
+    assert order.tolist() == expect_order
