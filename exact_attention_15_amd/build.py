@@ -11,6 +11,9 @@ ROOT = os.path.dirname(HERE)
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libexattn.so")
 SOURCES = ["abi.hip", "mask.hip", "fwd.hip", "decode.hip"]
+# The forward kernel relies on no NaN semantics (masked scores are -inf), so
+# it drops IEEE NaN quieting: max/min then need no canonicalising moves.
+EXTRA = {"fwd.hip": ["-mno-amdgpu-ieee", "-fno-honor-nans"]}
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 FLAGS = [
@@ -23,7 +26,7 @@ FLAGS = [
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *FLAGS, *EXTRA.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")

@@ -122,6 +122,8 @@ attn_status attn_fwd(attn_tensor q, attn_tensor k, attn_tensor v, attn_tensor o,
     if ((st = check_tensor(v, "v", true)) != ATTN_OK) return st;
     if ((st = check_tensor(o, "o", true)) != ATTN_OK) return st;
     if (!lse) return fail(ATTN_ERR_INVALID, "attn_fwd: null lse");
+    if (k.stride_n >= (int64_t(1) << 24) || v.stride_n >= (int64_t(1) << 24))
+        return fail(ATTN_ERR_UNSUPPORTED, "attn_fwd: k/v token stride must be below 2^24 elements");
     const MaskLayout L = mask_layout(B, N);
     if (int64_t(B) * L.nqt * Hq > 0x7FFFFFFFLL) return fail(ATTN_ERR_UNSUPPORTED, "attn_fwd: grid too large");
     const attn_mask_spec sp = spec_or_default(spec);
@@ -150,9 +152,9 @@ attn_status attn_fwd(attn_tensor q, attn_tensor k, attn_tensor v, attn_tensor o,
     const float log2e = 1.4426950408889634f;
     p.scale_log2 = scale * log2e;
     const bool softcap = sp.flags & ATTN_MOD_SOFTCAP;
-    p.softcap = softcap ? sp.softcap : 0.f;
-    p.cap_inv_scale = softcap ? scale / sp.softcap : 0.f;
+    p.cap_inv_scale_2log2e = softcap ? 2.f * log2e * (scale / sp.softcap) : 0.f;
     p.cap_log2 = softcap ? sp.softcap * log2e : 0.f;
+    p.cap_log2_2 = 2.f * p.cap_log2;
     p.mask = mask_view(mask, L);
     hipError_t e = launch_fwd(p, d, softcap, s);
     if (e != hipSuccess) return hip_fail(e, "attn_fwd");

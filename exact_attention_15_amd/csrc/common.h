@@ -71,9 +71,9 @@ struct FwdParams {
     int64_t o_sb, o_sh, o_sn;
     int B, Hq, Hkv, N, nqt, nkt;
     float scale_log2;    // scale * log2(e): scores in base-2 units
-    float softcap;       // cap c (softcap mode only)
-    float cap_inv_scale; // scale / c (softcap mode only)
-    float cap_log2;      // c * log2(e) (softcap mode only)
+    float cap_inv_scale_2log2e; // 2 * log2(e) * scale / c (softcap mode only)
+    float cap_log2;             // c * log2(e)     (softcap mode only)
+    float cap_log2_2;           // 2 * c * log2(e) (softcap mode only)
     MaskView mask;
 };
 

@@ -11,53 +11,76 @@
 // page: normalise once at the end, parallelise over query tiles, and keep
 // each wave's rows private so waves never reduce through shared memory).
 //
+// Data movement.  K and V tiles go from HBM straight into LDS with
+// global_load_lds_dwordx4 (no register staging, no VALU work): every wave
+// instruction writes 1 KiB of LDS contiguously, lane l at byte 16*l.  Rows
+// are not padded; instead the 16-byte chunks of row r are XOR-swizzled
+// (chunk c stored at c ^ swz(r)), which the loading lanes realise by picking
+// which global chunk they fetch.  The next tile is requested before the
+// current one is consumed, so its latency hides behind a tile of MFMA work.
+//
 // MFMA formulation.  Scores are computed transposed, S^T = K Q^T, with
-// v_mfma_f32_32x32x16_bf16: K rows are the A operand (read from LDS), the
-// wave's 32 query rows are the B operand (held in registers for the whole
+// v_mfma_f32_32x32x16_bf16: K rows are the A operand (ds_read_b128 from LDS),
+// the wave's 32 query rows are the B operand (held in registers for the whole
 // kernel).  In the 32x32 accumulator, lane l holds column l%32 -- one query
 // -- and 16 keys, so a row's max and sum need only an in-lane reduction and
-// one exchange between the two 32-lane halves.  The output is accumulated
-// transposed too, O^T = V^T P^T: the probabilities already sit in the B
-// operand layout (lane = query, register = key), and V^T is the A operand,
-// read from a transposed copy of the V tile in LDS.
+// one exchange between the two 32-lane halves (v_permlane32_swap).  The
+// output is accumulated transposed too, O^T = V^T P^T: the probabilities
+// already sit in the B-operand layout (lane = query, register = key), and
+// the V^T operand is read from the row-major V tile with the LDS transpose
+// read ds_read_b64_tr_b16.
 //
-// Scores are kept in base-2 units (scale * log2 e folded in), so every
-// exponential is one v_exp_f32.
+// Scores are kept in base-2 units (scale * log2 e folded into one FMA), so
+// every exponential is one v_exp_f32.
 #include "common.h"
 
 namespace exattn {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
 
-constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
+// Lazy rescaling threshold (base-2 units): probabilities stay <= 2^8.
+constexpr float RESCALE_LOG2 = 8.f;
 
 template <int D> struct FwdCfg {
-    static constexpr int KSTEPS = D / 16;            // k-steps of the S^T MFMAs
-    static constexpr int DBLK = D / 32;              // 32-row blocks of O^T
-    static constexpr int K_ROW = D + 8;              // K tile row stride in LDS (elements)
-    static constexpr int VT_ROW = BLOCK_N + 4;       // V^T tile row stride in LDS (elements)
-    static constexpr int K_ELEMS = BLOCK_N * K_ROW;
-    static constexpr int VT_ELEMS = D * VT_ROW;
-    static constexpr int STAGE = K_ELEMS + VT_ELEMS; // one buffer, elements
-    static constexpr int CHUNKS = D / 8;             // 16-byte chunks per row
-    static constexpr int K_LOADS = BLOCK_N * CHUNKS / 256;       // per thread
-    static constexpr int V_ITEMS = (BLOCK_N / 2) * CHUNKS / 256; // row pairs per thread
-    static constexpr size_t LDS_BYTES = size_t(2) * STAGE * 2;
+    static constexpr int KSTEPS = D / 16;              // k-steps of the S^T MFMAs
+    static constexpr int DBLK = D / 32;                // 32-row blocks of O^T
+    static constexpr int ROW_BYTES = D * 2;            // one K or V row
+    static constexpr int CHUNKS = D / 8;               // 16-byte chunks per row
+    static constexpr int TILE_BYTES = BLOCK_N * ROW_BYTES;
+    static constexpr int STAGE_BYTES = 2 * TILE_BYTES; // K tile + V tile
+    static constexpr int LOADS = TILE_BYTES / 1024 / 4; // 1 KiB loads per wave per tile
+    static constexpr int ROWS_PER_LOAD = 1024 / ROW_BYTES;
+    static constexpr size_t LDS_BYTES = size_t(2) * STAGE_BYTES;
 };
+
+// Chunk swizzle.  D = 128 (16 chunks per row; 4 rows span the 64 banks):
+// swz(r) = 4*(r%4) + (r/4)%4 gives 16 consecutive rows distinct values
+// (conflict-free K reads of one chunk column) and gives 4 consecutive rows
+// disjoint groups of 4 chunks (conflict-free transpose reads of V).  D = 64
+// (8 chunks per row; two rows span the banks): the same two properties with
+// swz(r) = 4*((r/2)%2) + (r/4)%4.
+template <int D> __device__ __forceinline__ int swz(int r) {
+    if constexpr (D == 128) return 4 * (r & 3) + ((r >> 2) & 3);
+    else return 4 * ((r >> 1) & 1) + ((r >> 2) & 3);
+}
 
 // 32x32 accumulator layout of v_mfma_f32_32x32x16_bf16: register r of lane l
 // holds row 8*(r/4) + 4*(l/32) + r%4 and column l%32.
 __device__ __forceinline__ int acc_row(int r, int half) { return 8 * (r >> 2) + 4 * half + (r & 3); }
 
-__device__ __forceinline__ float wave_swap_halves(float x) {
-    // Value of lane l^32 (the other 32-lane half of the wave).
-    return __shfl_xor(x, 32);
+__device__ __forceinline__ float wave_swap_halves(float x, int half) {
+    // Value of lane l^32 (the other 32-lane half of the wave): after
+    // v_permlane32_swap(x, x) the first result holds the low half twice and
+    // the second the high half twice.
+    const uint32_t u = __builtin_bit_cast(uint32_t, x);
+    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    return __builtin_bit_cast(float, half ? r[0] : r[1]);
 }
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
@@ -67,10 +90,19 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
     return __builtin_bit_cast(uint32_t, v);
 }
 
+__device__ __forceinline__ u32x2_t lds_read_tr16(const lds_u8 *base, int off) {
+    // ds_read_b64_tr_b16: within each 16-lane group, element e of lane i is
+    // element i%4 of the 8 bytes addressed by lane 4e + i/4.
+    const i16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        reinterpret_cast<__attribute__((address_space(3))) i16x4_t *>(const_cast<lds_u8 *>(base) + off));
+    return __builtin_bit_cast(u32x2_t, v);
+}
+
 template <int D, bool SOFTCAP>
 __global__ __launch_bounds__(256, 2) void k_attn_fwd(FwdParams p) {
     using C = FwdCfg<D>;
-    extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
+    extern __shared__ __attribute__((aligned(1024))) uint8_t smem_raw[];
+    lds_u8 *smem = (lds_u8 *)(smem_raw); // generic -> LDS address space
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63;
@@ -106,105 +138,102 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd(FwdParams p) {
     const uint16_t *kbase = p.k + b * p.k_sb + hk * p.k_sh;
     const uint16_t *vbase = p.v + b * p.v_sb + hk * p.v_sh;
 
+    // ---- HBM -> LDS tile loads ----
+    // Wave w, load u fills LDS bytes [(LOADS*w + u) KiB, +1 KiB) of a tile:
+    // row ROWS_PER_LOAD*(LOADS*w + u) + lane/CHUNKS, physical chunk
+    // lane%CHUNKS, which holds logical chunk (lane%CHUNKS) ^ swz(row).
+    int ld_row[C::LOADS];
+    uint32_t ld_col[C::LOADS]; // element offset of the fetched chunk
+#pragma unroll
+    for (int u = 0; u < C::LOADS; ++u) {
+        const int r = C::ROWS_PER_LOAD * (C::LOADS * wave + u) + lane / C::CHUNKS;
+        ld_row[u] = r;
+        ld_col[u] = 8u * uint32_t((lane % C::CHUNKS) ^ swz<D>(r));
+    }
+    auto issue_tile = [&](int kt, int stage) {
+        const int key0 = kt * BLOCK_N;
+        const int last = p.N - 1 - key0; // rows past N re-read row N-1 (always masked)
+        lds_u8 *kdst = smem + stage * C::STAGE_BYTES;
+        lds_u8 *vdst = kdst + C::TILE_BYTES;
+#pragma unroll
+        for (int u = 0; u < C::LOADS; ++u) {
+            const int r = min(ld_row[u], last);
+            const uint16_t *ksrc = kbase + int64_t(key0 + r) * p.k_sn + ld_col[u];
+            const uint16_t *vsrc = vbase + int64_t(key0 + r) * p.v_sn + ld_col[u];
+            const int off = (C::LOADS * wave + u) * 1024;
+            __builtin_amdgcn_global_load_lds(ksrc, kdst + off, 16, 0, 0);
+            __builtin_amdgcn_global_load_lds(vsrc, vdst + off, 16, 0, 0);
+        }
+    };
+
+    // ---- per-lane LDS read offsets ----
+    // K (A operand of S^T): lane reads row 32*kb + col, logical chunk 2s + half.
+    int k_rd[2][C::KSTEPS];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int s = 0; s < C::KSTEPS; ++s) {
+            const int r = 32 * kb + col;
+            k_rd[kb][s] = r * C::ROW_BYTES + 16 * ((2 * s + half) ^ swz<D>(r));
+        }
+    // V (A operand of O^T, via transpose reads): for the probabilities of
+    // keys k0..k0+3 and d-block db, lane reads 8 bytes of row k0 + (lane%16)/4
+    // at elements 32*db + 16*dh + 4*(lane%4); the transpose read then returns,
+    // in element e, V[k0+e] at column 32*db + lane%32.
+    const int s16 = lane & 15, dh = (lane >> 4) & 1;
+    auto v_rd = [&](int k0, int db) {
+        const int r = k0 + (s16 >> 2);
+        const int cb = 64 * db + 32 * dh + 8 * (s16 & 3); // byte offset inside the row
+        return r * C::ROW_BYTES + 16 * ((cb >> 4) ^ swz<D>(r)) + (cb & 15);
+    };
+
     f32x16_t acc_o[C::DBLK];
 #pragma unroll
     for (int i = 0; i < C::DBLK; ++i) acc_o[i] = f32x16_t{};
-    float m_run = -INFINITY; // running max (base-2 units), shared by both halves
+    float m_run = -INFINITY; // reference max (base-2 units), shared by both halves
     float l_run = 0.f;       // this half's share of the running sum
 
-    // Register staging of the next tile.
-    u32x4_t kreg[C::K_LOADS];
-    u32x4_t vreg[C::V_ITEMS][2];
-
-    auto gload = [&](int kt) {
-        const int key0 = kt * BLOCK_N;
-#pragma unroll
-        for (int u = 0; u < C::K_LOADS; ++u) {
-            const int ci = tid + 256 * u;
-            const int key = ci / C::CHUNKS, c = ci % C::CHUNKS;
-            const int gk = key0 + key;
-            u32x4_t x = {0u, 0u, 0u, 0u};
-            if (gk < p.N) x = *reinterpret_cast<const u32x4_t *>(kbase + int64_t(gk) * p.k_sn + 8 * c);
-            kreg[u] = x;
-        }
-#pragma unroll
-        for (int u = 0; u < C::V_ITEMS; ++u) {
-            const int it = tid + 256 * u;
-            const int pr = it % (BLOCK_N / 2), c = it / (BLOCK_N / 2);
-            const int gk = key0 + 2 * pr;
-            u32x4_t x0 = {0u, 0u, 0u, 0u}, x1 = {0u, 0u, 0u, 0u};
-            if (gk < p.N) x0 = *reinterpret_cast<const u32x4_t *>(vbase + int64_t(gk) * p.v_sn + 8 * c);
-            if (gk + 1 < p.N) x1 = *reinterpret_cast<const u32x4_t *>(vbase + int64_t(gk + 1) * p.v_sn + 8 * c);
-            vreg[u][0] = x0;
-            vreg[u][1] = x1;
-        }
-    };
-    auto swrite = [&](int stage) {
-        uint16_t *ks = smem + stage * C::STAGE;
-        uint16_t *vts = ks + C::K_ELEMS;
-#pragma unroll
-        for (int u = 0; u < C::K_LOADS; ++u) {
-            const int ci = tid + 256 * u;
-            const int key = ci / C::CHUNKS, c = ci % C::CHUNKS;
-            *reinterpret_cast<u32x4_t *>(ks + key * C::K_ROW + 8 * c) = kreg[u];
-        }
-        // V^T[d][key]: pair keys (2pr, 2pr+1) of the same d into one dword.
-#pragma unroll
-        for (int u = 0; u < C::V_ITEMS; ++u) {
-            const int it = tid + 256 * u;
-            const int pr = it % (BLOCK_N / 2), c = it / (BLOCK_N / 2);
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const uint32_t a = vreg[u][0][j >> 1], bb = vreg[u][1][j >> 1];
-                const uint32_t w = (j & 1) ? ((a >> 16) | (bb & 0xFFFF0000u))
-                                           : ((a & 0xFFFFu) | (bb << 16));
-                *reinterpret_cast<uint32_t *>(vts + (8 * c + j) * C::VT_ROW + 2 * pr) = w;
-            }
-        }
-    };
-
-    if (ntiles > 0) {
-        gload(tiles[0] >> 1);
-        swrite(0);
-    }
+    if (ntiles > 0) issue_tile(tiles[0] >> 1, 0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
 
     for (int it = 0; it < ntiles; ++it) {
         const int ent = tiles[it];
         const int kt = ent >> 1;
         const bool partial = ent & TILE_PARTIAL;
-        if (it + 1 < ntiles) gload(tiles[it + 1] >> 1);
+        // The other buffer was last read in iteration it-1, which every wave
+        // has finished (barrier below), so it can be refilled now.
+        if (it + 1 < ntiles) issue_tile(tiles[it + 1] >> 1, (it + 1) & 1);
 
-        const uint16_t *ks = smem + (it & 1) * C::STAGE;
-        const uint16_t *vts = ks + C::K_ELEMS;
+        const lds_u8 *ks = smem + (it & 1) * C::STAGE_BYTES;
+        const lds_u8 *vs = ks + C::TILE_BYTES;
 
         // ---- S^T = K Q^T for the tile's two 32-key blocks ----
         f32x16_t s0 = f32x16_t{}, s1 = f32x16_t{};
 #pragma unroll
         for (int s = 0; s < C::KSTEPS; ++s) {
-            const bf16x8_t a0 = *reinterpret_cast<const bf16x8_t *>(ks + col * C::K_ROW + 16 * s + 8 * half);
-            const bf16x8_t a1 = *reinterpret_cast<const bf16x8_t *>(ks + (32 + col) * C::K_ROW + 16 * s + 8 * half);
+            const bf16x8_t a0 = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8_t *>(ks + k_rd[0][s]);
+            const bf16x8_t a1 = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8_t *>(ks + k_rd[1][s]);
             s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf[s], s0, 0, 0, 0);
             s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qf[s], s1, 0, 0, 0);
         }
 
         // ---- score_mod and mask in registers ----
+        // Without a cap the raw dot products are kept and the scale is folded
+        // into the exponent's FMA (max commutes with a positive scale); with
+        // the cap, c * tanh(scale * s / c) is formed first, in base-2 units,
+        // using tanh(x) = 1 - 2 / (exp(2x) + 1).
         float t[32];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             t[r] = s0[r];
             t[16 + r] = s1[r];
         }
+        if constexpr (SOFTCAP) {
 #pragma unroll
-        for (int j = 0; j < 32; ++j) {
-            if constexpr (SOFTCAP) {
-                // c * tanh(scale * s / c) with tanh(x) = 1 - 2 / (exp(2x) + 1),
-                // then to base-2 units.
-                const float e = __builtin_amdgcn_exp2f(t[j] * (p.cap_inv_scale * 2.f * LOG2E));
-                const float th = 1.f - 2.f * __builtin_amdgcn_rcpf(e + 1.f);
-                t[j] = th * p.cap_log2;
-            } else {
-                t[j] *= p.scale_log2;
+            for (int j = 0; j < 32; ++j) {
+                const float e = __builtin_amdgcn_exp2f(t[j] * p.cap_inv_scale_2log2e);
+                t[j] = p.cap_log2 - p.cap_log2_2 * __builtin_amdgcn_rcpf(e + 1.f);
             }
         }
         if (partial) {
@@ -217,23 +246,36 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd(FwdParams p) {
         }
 
         // ---- online softmax ----
-        float mt = t[0];
+        float mt = fmaxf(t[0], t[1]);
 #pragma unroll
-        for (int j = 1; j < 32; ++j) mt = fmaxf(mt, t[j]);
-        mt = fmaxf(mt, wave_swap_halves(mt));
+        for (int j = 2; j < 32; j += 2) mt = fmaxf(mt, fmaxf(t[j], t[j + 1]));
+        mt = fmaxf(mt, wave_swap_halves(mt, half));
+        if constexpr (!SOFTCAP) mt *= p.scale_log2;
+        // Rescale O and l only when some valid row's max grew by more than
+        // RESCALE_LOG2 (a wave-uniform decision); otherwise keep the older,
+        // smaller reference max: p stays <= 2^RESCALE_LOG2 and the result is
+        // exact, since O, l and the LSE all use the same reference.  Rows
+        // past N never vote, so the decision does not depend on whether
+        // fully visible tiles are element-masked.
         const float m_new = fmaxf(m_run, mt);
-        const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-        m_run = m_new;
+        if (__any(row_ok && m_new > m_run + RESCALE_LOG2)) {
+            const float alpha = __builtin_amdgcn_exp2f(m_run - (m_new == -INFINITY ? 0.f : m_new));
+            l_run *= alpha;
+#pragma unroll
+            for (int i = 0; i < C::DBLK; ++i) acc_o[i] *= alpha;
+            m_run = m_new;
+        }
+        const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
         float psum = 0.f;
 #pragma unroll
         for (int j = 0; j < 32; ++j) {
-            t[j] = __builtin_amdgcn_exp2f(t[j] - m_use);
+            if constexpr (SOFTCAP)
+                t[j] = __builtin_amdgcn_exp2f(t[j] - m_use);
+            else
+                t[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(t[j], p.scale_log2, -m_use));
             psum += t[j];
         }
-        l_run = l_run * alpha + psum;
-#pragma unroll
-        for (int i = 0; i < C::DBLK; ++i) acc_o[i] *= alpha;
+        l_run += psum;
 
         // ---- O^T += V^T P^T ----
 #pragma unroll
@@ -247,26 +289,27 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd(FwdParams p) {
                 pk[2] = pack_bf16x2(t[base + 4], t[base + 5]);
                 pk[3] = pack_bf16x2(t[base + 6], t[base + 7]);
                 const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, pk);
-                // Keys of these 8 probabilities: key0 + {0..3} and key0 + 8 + {0..3}.
-                const int key0 = 32 * kb + 16 * hh + 4 * half;
+                // Keys of these 8 probabilities: k0 + {0..3} and k0 + 8 + {0..3}.
+                const int k0 = 32 * kb + 16 * hh + 4 * half;
 #pragma unroll
                 for (int db = 0; db < C::DBLK; ++db) {
-                    const uint16_t *vp = vts + (32 * db + col) * C::VT_ROW + key0;
-                    const u32x2_t lo4 = *reinterpret_cast<const u32x2_t *>(vp);
-                    const u32x2_t hi4 = *reinterpret_cast<const u32x2_t *>(vp + 8);
-                    const u32x4_t av = {lo4[0], lo4[1], hi4[0], hi4[1]};
+                    const u32x2_t l2 = lds_read_tr16(vs, v_rd(k0, db));
+                    const u32x2_t h2 = lds_read_tr16(vs, v_rd(k0 + 8, db));
+                    const u32x4_t av = {l2[0], l2[1], h2[0], h2[1]};
                     acc_o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
                         __builtin_bit_cast(bf16x8_t, av), pb, acc_o[db], 0, 0, 0);
                 }
             }
         }
 
-        if (it + 1 < ntiles) swrite((it + 1) & 1);
+        // The next tile's LDS writes must land before anyone reads them, and
+        // this tile's buffer must be free before it is refilled.
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
     }
 
     // ---- epilogue: O / l, LSE = ln 2 * (m + log2 l) ----
-    const float l_tot = l_run + wave_swap_halves(l_run);
+    const float l_tot = l_run + wave_swap_halves(l_run, half);
     if (row_ok) {
         const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
         uint16_t *orow = p.o + b * p.o_sb + h * p.o_sh + int64_t(row) * p.o_sn;
@@ -290,7 +333,6 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd(FwdParams p) {
 
 template <int D, bool SOFTCAP> static hipError_t launch_fwd_t(const FwdParams &p, hipStream_t stream) {
     using C = FwdCfg<D>;
-    // More than 64 KiB of dynamic LDS must be allowed explicitly (per device).
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&k_attn_fwd<D, SOFTCAP>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize,
                                        int(C::LDS_BYTES));
@@ -305,5 +347,8 @@ hipError_t launch_fwd(const FwdParams &p, int d, bool softcap, hipStream_t strea
     if (d == 128) return softcap ? launch_fwd_t<128, true>(p, stream) : launch_fwd_t<128, false>(p, stream);
     return softcap ? launch_fwd_t<64, true>(p, stream) : launch_fwd_t<64, false>(p, stream);
 }
+
+static_assert(FwdCfg<128>::LOADS == 4 && FwdCfg<64>::LOADS == 2, "tile loads per wave");
+static_assert(FwdCfg<128>::LDS_BYTES == 65536, "two 32 KiB stages at d = 128");
 
 } // namespace exattn
