@@ -265,6 +265,9 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--configs", default="1,2,3,4,5")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only run one device-to-device copy of MIB MiB (a known-size "
+                         "kernel for scaling the HBM byte counters), then exit")
     args = ap.parse_args(argv)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: the forward and decode kernels run on a single "
@@ -277,6 +280,15 @@ def main(argv=None):
         print("bench.py needs a GPU", file=sys.stderr)
         return 1
     dev = torch.device("cuda", 0)
+    if args.calibrate_copy:
+        n = args.calibrate_copy << 20
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes": n}))
+        return 0
     ea.library()
     cfg_ids = [int(x) for x in args.configs.split(",") if x]
 

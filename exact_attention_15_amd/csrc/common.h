@@ -37,7 +37,7 @@ inline MaskLayout mask_layout(int B, int N) {
     L.off_hi = off;    off = align256(off + 4 * rows);
     L.off_count = off; off = align256(off + 4 * items);
     L.off_list = off;  off = align256(off + 4 * items * size_t(L.nkt));
-    L.off_order = off; off = align256(off + 4 * items);
+    L.off_order = off; off = align256(off + 4 * items); // [B][nqt]
     L.bytes = off;
     return L;
 }

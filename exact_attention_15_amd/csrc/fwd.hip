@@ -108,10 +108,28 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd(FwdParams p) {
     const int wave = tid >> 6, lane = tid & 63;
     const int col = lane & 31, half = lane >> 5;
 
-    const int item = p.mask.order[blockIdx.x / p.Hq];
-    const int h = blockIdx.x % p.Hq;
-    const int b = item / p.nqt, qt = item % p.nqt;
-    const int hk = h / (p.Hq / p.Hkv);
+    // Work assignment.  A "group" is everything that reads the same K/V:
+    // one (batch row, KV head) with all its query tiles and all Hq/Hkv query
+    // heads, ordered heavy-first by query tile, heads adjacent.  Workgroups
+    // are dispatched round-robin over the 8 XCDs (id % 8), each with its own
+    // L2, so group g is given to XCD g % 8: an XCD then streams whole groups
+    // and their K/V tiles are fetched into its L2 once and reused there.
+    const int G = p.Hq / p.Hkv;
+    const int per_group = G * p.nqt;
+    const int ngroups = p.B * p.Hkv;
+    int group, within;
+    if ((ngroups & 7) == 0) {
+        const int x = blockIdx.x & 7, j = blockIdx.x >> 3;
+        group = x + 8 * (j / per_group);
+        within = j % per_group;
+    } else {
+        group = blockIdx.x / per_group;
+        within = blockIdx.x % per_group;
+    }
+    const int b = group / p.Hkv, hk = group % p.Hkv;
+    const int qt = p.mask.order[int64_t(b) * p.nqt + within / G];
+    const int h = hk * G + within % G;
+    const int item = b * p.nqt + qt;
     const int row = qt * BLOCK_M + wave * 32 + col; // this lane's query row
     const bool row_ok = row < p.N;
 

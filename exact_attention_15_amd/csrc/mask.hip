@@ -1,5 +1,6 @@
 // Block-mask builder: per-row visible key intervals, per-query-tile lists of
-// visited key tiles (FULL or PARTIAL), and a heavy-first work order.
+// visited key tiles (FULL or PARTIAL), and a heavy-first order of the query
+// tiles of each batch row.
 //
 // Every mask the library supports (causal, sliding window, document
 // boundaries, and their combinations) leaves each query row i one interval
@@ -70,7 +71,8 @@ __global__ __launch_bounds__(256) void k_mask_tiles(uint32_t flags, int N, int n
     const bool no_skip = flags & ATTN_MASK_NO_SKIP;
     const int per = (nkt + 255) / 256;
     const int kt0 = min(nkt, t * per), kt1 = min(nkt, kt0 + per);
-    // At most `per` tiles per thread; keep their classes in a bit list.
+    // Count this thread's visited tiles; the classification is repeated in
+    // the write pass below (it is cheap) instead of being stored.
     int n_mine = 0;
     for (int kt = kt0; kt < kt1; ++kt) {
         const int c0 = kt * BLOCK_N, c1 = c0 + BLOCK_N - 1;
@@ -112,17 +114,21 @@ __global__ __launch_bounds__(256) void k_mask_tiles(uint32_t flags, int N, int n
     if (t == 255) count_out[item] = s_cnt[255];
 }
 
-// Single workgroup: order[rank] = item, ranked by descending tile count
-// (ties keep item order), so the heaviest query tiles are dispatched first.
-__global__ __launch_bounds__(1024) void k_mask_order(int n, const int32_t *count, int32_t *order) {
-    for (int i = threadIdx.x; i < n; i += blockDim.x) {
-        const int ci = count[i];
+// One workgroup per batch row: order[b][rank] = query tile, ranked by
+// descending visited-tile count (ties keep tile order), so the forward
+// kernel can hand out the heaviest query tiles of each batch row first.
+__global__ __launch_bounds__(1024) void k_mask_order(int nqt, const int32_t *count, int32_t *order) {
+    const int b = blockIdx.x;
+    const int32_t *cb = count + int64_t(b) * nqt;
+    int32_t *ob = order + int64_t(b) * nqt;
+    for (int i = threadIdx.x; i < nqt; i += blockDim.x) {
+        const int ci = cb[i];
         int rank = 0;
-        for (int j = 0; j < n; ++j) {
-            const int cj = count[j];
+        for (int j = 0; j < nqt; ++j) {
+            const int cj = cb[j];
             rank += (cj > ci) || (cj == ci && j < i);
         }
-        order[rank] = i;
+        ob[rank] = i;
     }
 }
 
@@ -144,7 +150,7 @@ hipError_t launch_mask_build(const attn_mask_spec &spec, const MaskLayout &L, vo
                        L.nqt, L.nkt, lo, hi, cnt, list);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k_mask_order, dim3(1), dim3(1024), 0, stream, L.B * L.nqt, cnt, order);
+    hipLaunchKernelGGL(k_mask_order, dim3(L.B), dim3(1024), 0, stream, L.nqt, cnt, order);
     return hipGetLastError();
 }
 

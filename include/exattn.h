@@ -88,7 +88,7 @@ typedef struct {
  * Block mask: per-row visible key intervals, and for every 128-query tile
  * the list of 64-key tiles that hold at least one visible key, each marked
  * FULL (no element mask needed) or PARTIAL, plus a heavy-first order of the
- * query tiles.  Fully masked tiles are never visited (it-trends-board
+ * query tiles of each batch row.  Fully masked tiles are never visited (it-trends-board
  * "PyTorch FlexAttention 도입 분석", section 2, the block-mask early-out;
  * youngju.dev "FlashAttention 논문 분석", FlashAttention-2 improvement 1:
  * blocks that need no mask skip the masking).

@@ -226,9 +226,10 @@ def test_mask_builder_matches_host(ea, kind, N):
             got = m["list"][b, qt, : len(expect)].numpy().tolist()
             assert m["count"][b, qt].item() == len(expect)
             assert got == expect, (b, qt)
-    # heavy-first order: a permutation, counts non-increasing, ties by index
-    order = m["order"].numpy()
-    flat = counts.reshape(-1)
-    assert sorted(order.tolist()) == list(range(B * nqt))
-    expect_order = sorted(range(B * nqt), key=lambda x: (-flat[x], x))
-    assert order.tolist() == expect_order
+    # heavy-first order per batch row: a permutation, counts non-increasing,
+    # ties by tile index
+    order = m["order"].numpy().reshape(B, nqt)
+    for b in range(B):
+        assert sorted(order[b].tolist()) == list(range(nqt))
+        expect_order = sorted(range(nqt), key=lambda x: (-counts[b, x], x))
+        assert order[b].tolist() == expect_order
