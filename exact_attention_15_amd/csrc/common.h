@@ -4,7 +4,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include "../../include/exattn.h"
+#include "exattn.h" // include/ is on the include path
 
 namespace exattn {
 

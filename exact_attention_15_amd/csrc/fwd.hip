@@ -46,6 +46,12 @@ typedef __attribute__((address_space(3))) uint8_t lds_u8;
 constexpr float LN2 = 0.6931471805599453f;
 // Lazy rescaling threshold (base-2 units): probabilities stay <= 2^8.
 constexpr float RESCALE_LOG2 = 8.f;
+// LDS operand reads in flight ahead of the MFMAs that consume them.
+constexpr int QK_AHEAD = 2;
+constexpr int PV_AHEAD = 3;
+// Instruction classes of __builtin_amdgcn_sched_group_barrier.
+constexpr int SCHED_MFMA = 0x0008;
+constexpr int SCHED_DS_READ = 0x0100;
 
 template <int D> struct FwdCfg {
     static constexpr int KSTEPS = D / 16;              // k-steps of the S^T MFMAs
@@ -98,10 +104,13 @@ __device__ __forceinline__ u32x2_t lds_read_tr16(const lds_u8 *base, int off) {
     return __builtin_bit_cast(u32x2_t, v);
 }
 
+extern __shared__ __attribute__((aligned(1024))) uint8_t smem_raw[];
+
+// The kernel body is a device template; the __global__ entry points below
+// are plain (non-template) functions, one per head dim and score mod.
 template <int D, bool SOFTCAP>
-__global__ __launch_bounds__(256, 2) void k_attn_fwd(FwdParams p) {
+__device__ __forceinline__ void attn_fwd_body(const FwdParams &p) {
     using C = FwdCfg<D>;
-    extern __shared__ __attribute__((aligned(1024))) uint8_t smem_raw[];
     lds_u8 *smem = (lds_u8 *)(smem_raw); // generic -> LDS address space
 
     const int tid = threadIdx.x;
@@ -127,7 +136,9 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd(FwdParams p) {
         within = blockIdx.x % per_group;
     }
     const int b = group / p.Hkv, hk = group % p.Hkv;
-    const int qt = p.mask.order[int64_t(b) * p.nqt + within / G];
+    // Values read from memory are not known to be wave-uniform; readfirstlane
+    // makes them scalars so all per-tile address arithmetic stays on the SALU.
+    const int qt = __builtin_amdgcn_readfirstlane(p.mask.order[int64_t(b) * p.nqt + within / G]);
     const int h = hk * G + within % G;
     const int item = b * p.nqt + qt;
     const int row = qt * BLOCK_M + wave * 32 + col; // this lane's query row
@@ -151,7 +162,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd(FwdParams p) {
         hi = p.mask.hi[int64_t(b) * p.N + row];
     }
 
-    const int ntiles = p.mask.count[item];
+    const int ntiles = __builtin_amdgcn_readfirstlane(p.mask.count[item]);
     const int32_t *tiles = p.mask.list + int64_t(item) * p.nkt;
     const uint16_t *kbase = p.k + b * p.k_sb + hk * p.k_sh;
     const uint16_t *vbase = p.v + b * p.v_sb + hk * p.v_sh;
@@ -159,51 +170,64 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd(FwdParams p) {
     // ---- HBM -> LDS tile loads ----
     // Wave w, load u fills LDS bytes [(LOADS*w + u) KiB, +1 KiB) of a tile:
     // row ROWS_PER_LOAD*(LOADS*w + u) + lane/CHUNKS, physical chunk
-    // lane%CHUNKS, which holds logical chunk (lane%CHUNKS) ^ swz(row).
-    int ld_row[C::LOADS];
-    uint32_t ld_col[C::LOADS]; // element offset of the fetched chunk
+    // lane%CHUNKS, which holds logical chunk (lane%CHUNKS) ^ swz(row).  The
+    // per-lane element offsets inside a tile fit 32 bits (stride_n < 2^24).
+    auto ld_row = [&](int u) { return C::ROWS_PER_LOAD * (C::LOADS * wave + u) + lane / C::CHUNKS; };
+    auto ld_col = [&](int u) { return 8u * uint32_t((lane % C::CHUNKS) ^ swz<D>(ld_row(u))); };
+    uint32_t ld_koff[C::LOADS], ld_voff[C::LOADS];
 #pragma unroll
     for (int u = 0; u < C::LOADS; ++u) {
-        const int r = C::ROWS_PER_LOAD * (C::LOADS * wave + u) + lane / C::CHUNKS;
-        ld_row[u] = r;
-        ld_col[u] = 8u * uint32_t((lane % C::CHUNKS) ^ swz<D>(r));
+        ld_koff[u] = uint32_t(ld_row(u)) * uint32_t(p.k_sn) + ld_col(u);
+        ld_voff[u] = uint32_t(ld_row(u)) * uint32_t(p.v_sn) + ld_col(u);
     }
-    auto issue_tile = [&](int kt, int stage) {
+    auto issue_tile = [&](int kt, const int stage) {
         const int key0 = kt * BLOCK_N;
-        const int last = p.N - 1 - key0; // rows past N re-read row N-1 (always masked)
-        lds_u8 *kdst = smem + stage * C::STAGE_BYTES;
+        const uint16_t *kt_base = kbase + int64_t(key0) * p.k_sn;
+        const uint16_t *vt_base = vbase + int64_t(key0) * p.v_sn;
+        lds_u8 *kdst = smem + stage * C::STAGE_BYTES + C::LOADS * wave * 1024;
         lds_u8 *vdst = kdst + C::TILE_BYTES;
+        if (key0 + BLOCK_N <= p.N) {
 #pragma unroll
-        for (int u = 0; u < C::LOADS; ++u) {
-            const int r = min(ld_row[u], last);
-            const uint16_t *ksrc = kbase + int64_t(key0 + r) * p.k_sn + ld_col[u];
-            const uint16_t *vsrc = vbase + int64_t(key0 + r) * p.v_sn + ld_col[u];
-            const int off = (C::LOADS * wave + u) * 1024;
-            __builtin_amdgcn_global_load_lds(ksrc, kdst + off, 16, 0, 0);
-            __builtin_amdgcn_global_load_lds(vsrc, vdst + off, 16, 0, 0);
+            for (int u = 0; u < C::LOADS; ++u) {
+                __builtin_amdgcn_global_load_lds(kt_base + ld_koff[u], kdst + u * 1024, 16, 0, 0);
+                __builtin_amdgcn_global_load_lds(vt_base + ld_voff[u], vdst + u * 1024, 16, 0, 0);
+            }
+        } else {
+            const int last = p.N - 1 - key0; // rows past N re-read row N-1 (always masked)
+#pragma unroll
+            for (int u = 0; u < C::LOADS; ++u) {
+                const int r = min(ld_row(u), last);
+                __builtin_amdgcn_global_load_lds(kt_base + int64_t(r) * p.k_sn + ld_col(u),
+                                                 kdst + u * 1024, 16, 0, 0);
+                __builtin_amdgcn_global_load_lds(vt_base + int64_t(r) * p.v_sn + ld_col(u),
+                                                 vdst + u * 1024, 16, 0, 0);
+            }
         }
     };
 
-    // ---- per-lane LDS read offsets ----
-    // K (A operand of S^T): lane reads row 32*kb + col, logical chunk 2s + half.
-    int k_rd[2][C::KSTEPS];
+    // ---- per-lane LDS read offsets (bytes, inside one tile) ----
+    // K (A operand of S^T): lane reads row 32*kb + col, logical chunk 2s + half;
+    // swz depends on row % 16 only, so kb just adds 32 rows.
+    int k_rd[C::KSTEPS];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int s = 0; s < C::KSTEPS; ++s) {
-            const int r = 32 * kb + col;
-            k_rd[kb][s] = r * C::ROW_BYTES + 16 * ((2 * s + half) ^ swz<D>(r));
-        }
+    for (int s = 0; s < C::KSTEPS; ++s)
+        k_rd[s] = col * C::ROW_BYTES + 16 * ((2 * s + half) ^ swz<D>(col));
     // V (A operand of O^T, via transpose reads): for the probabilities of
-    // keys k0..k0+3 and d-block db, lane reads 8 bytes of row k0 + (lane%16)/4
-    // at elements 32*db + 16*dh + 4*(lane%4); the transpose read then returns,
-    // in element e, V[k0+e] at column 32*db + lane%32.
+    // keys k0..k0+3 (k0 = 32kb + 16hh + 4*half + 8j) and d-block db, lane
+    // reads 8 bytes of row k0 + (lane%16)/4 at elements 32*db + 16*dh +
+    // 4*(lane%4); the transpose read then returns, in element e, V[k0+e] at
+    // column 32*db + lane%32.  swz of those rows depends on (lane, j) only,
+    // so (kb, hh) just add 32kb + 16hh rows.
     const int s16 = lane & 15, dh = (lane >> 4) & 1;
-    auto v_rd = [&](int k0, int db) {
-        const int r = k0 + (s16 >> 2);
-        const int cb = 64 * db + 32 * dh + 8 * (s16 & 3); // byte offset inside the row
-        return r * C::ROW_BYTES + 16 * ((cb >> 4) ^ swz<D>(r)) + (cb & 15);
-    };
+    int v_rd[2][C::DBLK];
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int db = 0; db < C::DBLK; ++db) {
+            const int r = 4 * half + 8 * j + (s16 >> 2);
+            const int cb = 64 * db + 32 * dh + 8 * (s16 & 3); // byte offset inside the row
+            v_rd[j][db] = r * C::ROW_BYTES + 16 * ((cb >> 4) ^ swz<D>(r)) + (cb & 15);
+        }
 
     f32x16_t acc_o[C::DBLK];
 #pragma unroll
@@ -211,29 +235,47 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd(FwdParams p) {
     float m_run = -INFINITY; // reference max (base-2 units), shared by both halves
     float l_run = 0.f;       // this half's share of the running sum
 
-    if (ntiles > 0) issue_tile(tiles[0] >> 1, 0);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-
-    for (int it = 0; it < ntiles; ++it) {
-        const int ent = tiles[it];
+    // One tile: compute on buffer `stage` while the next tile (if any)
+    // streams into the other buffer.  The loop below is unrolled by two and
+    // the lambda is inlined with stage = 0 and 1, so every LDS address folds
+    // into a per-lane register plus an immediate offset.
+    auto step = [&](int it, const int stage) {
+        const int ent = __builtin_amdgcn_readfirstlane(tiles[it]);
         const int kt = ent >> 1;
         const bool partial = ent & TILE_PARTIAL;
         // The other buffer was last read in iteration it-1, which every wave
-        // has finished (barrier below), so it can be refilled now.
-        if (it + 1 < ntiles) issue_tile(tiles[it + 1] >> 1, (it + 1) & 1);
+        // has finished (barrier at the end of it), so it can be refilled now.
+        if (it + 1 < ntiles) issue_tile(__builtin_amdgcn_readfirstlane(tiles[it + 1]) >> 1, 1 - stage);
 
-        const lds_u8 *ks = smem + (it & 1) * C::STAGE_BYTES;
+        const lds_u8 *ks = smem + stage * C::STAGE_BYTES;
         const lds_u8 *vs = ks + C::TILE_BYTES;
 
         // ---- S^T = K Q^T for the tile's two 32-key blocks ----
+        // The K operands are read QK_AHEAD k-steps ahead of the MFMAs that
+        // use them, so LDS latency overlaps matrix work; the scheduling
+        // groups pin that interleave (DS reads, then MFMAs, k-step by k-step).
         f32x16_t s0 = f32x16_t{}, s1 = f32x16_t{};
+        {
+            bf16x8_t ka[C::KSTEPS][2];
+            auto kread = [&](int s) {
+                ka[s][0] = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8_t *>(ks + k_rd[s]);
+                ka[s][1] = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8_t *>(
+                    ks + k_rd[s] + 32 * C::ROW_BYTES);
+            };
 #pragma unroll
-        for (int s = 0; s < C::KSTEPS; ++s) {
-            const bf16x8_t a0 = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8_t *>(ks + k_rd[0][s]);
-            const bf16x8_t a1 = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8_t *>(ks + k_rd[1][s]);
-            s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf[s], s0, 0, 0, 0);
-            s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qf[s], s1, 0, 0, 0);
+            for (int s = 0; s < QK_AHEAD; ++s) kread(s);
+#pragma unroll
+            for (int s = 0; s < C::KSTEPS; ++s) {
+                if (s + QK_AHEAD < C::KSTEPS) kread(s + QK_AHEAD);
+                s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[s][0], qf[s], s0, 0, 0, 0);
+                s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[s][1], qf[s], s1, 0, 0, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(SCHED_DS_READ, 2 * QK_AHEAD, 0);
+#pragma unroll
+            for (int s = 0; s < C::KSTEPS; ++s) {
+                if (s + QK_AHEAD < C::KSTEPS) __builtin_amdgcn_sched_group_barrier(SCHED_DS_READ, 2, 0);
+                __builtin_amdgcn_sched_group_barrier(SCHED_MFMA, 2, 0);
+            }
         }
 
         // ---- score_mod and mask in registers ----
@@ -296,27 +338,43 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd(FwdParams p) {
         l_run += psum;
 
         // ---- O^T += V^T P^T ----
+        u32x4_t pk[4];
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
+        for (int i = 0; i < 4; ++i) {
+            pk[i][0] = pack_bf16x2(t[8 * i + 0], t[8 * i + 1]);
+            pk[i][1] = pack_bf16x2(t[8 * i + 2], t[8 * i + 3]);
+            pk[i][2] = pack_bf16x2(t[8 * i + 4], t[8 * i + 5]);
+            pk[i][3] = pack_bf16x2(t[8 * i + 6], t[8 * i + 7]);
+        }
+        // MFMA m = (2*kb + hh)*DBLK + db uses the probabilities of keys
+        // k0 + {0..3} and k0 + 8 + {0..3}, k0 = 32kb + 16hh + 4*half, and the
+        // V^T operand of those keys for d-block db; operands are read PV_AHEAD
+        // MFMAs ahead.
+        {
+            constexpr int NM = 4 * C::DBLK;
+            u32x4_t va[NM];
+            auto vread = [&](int m) {
+                const int kbhh = m / C::DBLK, db = m % C::DBLK;
+                const lds_u8 *vrow = vs + 16 * kbhh * C::ROW_BYTES;
+                const u32x2_t l2 = lds_read_tr16(vrow, v_rd[0][db]);
+                const u32x2_t h2 = lds_read_tr16(vrow, v_rd[1][db]);
+                va[m] = u32x4_t{l2[0], l2[1], h2[0], h2[1]};
+            };
 #pragma unroll
-            for (int hh = 0; hh < 2; ++hh) {
-                const int base = 16 * kb + 8 * hh;
-                u32x4_t pk;
-                pk[0] = pack_bf16x2(t[base + 0], t[base + 1]);
-                pk[1] = pack_bf16x2(t[base + 2], t[base + 3]);
-                pk[2] = pack_bf16x2(t[base + 4], t[base + 5]);
-                pk[3] = pack_bf16x2(t[base + 6], t[base + 7]);
-                const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, pk);
-                // Keys of these 8 probabilities: k0 + {0..3} and k0 + 8 + {0..3}.
-                const int k0 = 32 * kb + 16 * hh + 4 * half;
+            for (int m = 0; m < PV_AHEAD; ++m) vread(m);
 #pragma unroll
-                for (int db = 0; db < C::DBLK; ++db) {
-                    const u32x2_t l2 = lds_read_tr16(vs, v_rd(k0, db));
-                    const u32x2_t h2 = lds_read_tr16(vs, v_rd(k0 + 8, db));
-                    const u32x4_t av = {l2[0], l2[1], h2[0], h2[1]};
-                    acc_o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                        __builtin_bit_cast(bf16x8_t, av), pb, acc_o[db], 0, 0, 0);
-                }
+            for (int m = 0; m < NM; ++m) {
+                if (m + PV_AHEAD < NM) vread(m + PV_AHEAD);
+                const int db = m % C::DBLK;
+                acc_o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                    __builtin_bit_cast(bf16x8_t, va[m]), __builtin_bit_cast(bf16x8_t, pk[m / C::DBLK]),
+                    acc_o[db], 0, 0, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(SCHED_DS_READ, 2 * PV_AHEAD, 0);
+#pragma unroll
+            for (int m = 0; m < NM; ++m) {
+                if (m + PV_AHEAD < NM) __builtin_amdgcn_sched_group_barrier(SCHED_DS_READ, 2, 0);
+                __builtin_amdgcn_sched_group_barrier(SCHED_MFMA, 1, 0);
             }
         }
 
@@ -324,6 +382,14 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd(FwdParams p) {
         // this tile's buffer must be free before it is refilled.
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
+    };
+
+    if (ntiles > 0) issue_tile(__builtin_amdgcn_readfirstlane(tiles[0]) >> 1, 0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    for (int it = 0; it < ntiles; it += 2) {
+        step(it, 0);
+        if (it + 1 < ntiles) step(it + 1, 1);
     }
 
     // ---- epilogue: O / l, LSE = ln 2 * (m + log2 l) ----
@@ -349,21 +415,29 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd(FwdParams p) {
     }
 }
 
-template <int D, bool SOFTCAP> static hipError_t launch_fwd_t(const FwdParams &p, hipStream_t stream) {
-    using C = FwdCfg<D>;
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&k_attn_fwd<D, SOFTCAP>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       int(C::LDS_BYTES));
+#define EXATTN_FWD_KERNEL(NAME, D, SOFTCAP)                                                    \
+    __global__ __launch_bounds__(256, 2) void NAME(FwdParams p) { attn_fwd_body<D, SOFTCAP>(p); }
+EXATTN_FWD_KERNEL(k_attn_fwd_d128, 128, false)
+EXATTN_FWD_KERNEL(k_attn_fwd_d128_softcap, 128, true)
+EXATTN_FWD_KERNEL(k_attn_fwd_d64, 64, false)
+EXATTN_FWD_KERNEL(k_attn_fwd_d64_softcap, 64, true)
+#undef EXATTN_FWD_KERNEL
+
+static hipError_t launch_kernel(void (*kernel)(FwdParams), size_t lds_bytes, const FwdParams &p,
+                                hipStream_t stream) {
+    // More than 64 KiB of dynamic LDS must be allowed explicitly (per device).
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kernel),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, int(lds_bytes));
     if (e != hipSuccess) return e;
     const int64_t nblocks = int64_t(p.B) * p.nqt * p.Hq;
-    hipLaunchKernelGGL((k_attn_fwd<D, SOFTCAP>), dim3(unsigned(nblocks)), dim3(256), C::LDS_BYTES,
-                       stream, p);
+    hipLaunchKernelGGL(kernel, dim3(unsigned(nblocks)), dim3(256), lds_bytes, stream, p);
     return hipGetLastError();
 }
 
 hipError_t launch_fwd(const FwdParams &p, int d, bool softcap, hipStream_t stream) {
-    if (d == 128) return softcap ? launch_fwd_t<128, true>(p, stream) : launch_fwd_t<128, false>(p, stream);
-    return softcap ? launch_fwd_t<64, true>(p, stream) : launch_fwd_t<64, false>(p, stream);
+    if (d == 128)
+        return launch_kernel(softcap ? k_attn_fwd_d128_softcap : k_attn_fwd_d128, FwdCfg<128>::LDS_BYTES, p, stream);
+    return launch_kernel(softcap ? k_attn_fwd_d64_softcap : k_attn_fwd_d64, FwdCfg<64>::LDS_BYTES, p, stream);
 }
 
 static_assert(FwdCfg<128>::LOADS == 4 && FwdCfg<64>::LOADS == 2, "tile loads per wave");
