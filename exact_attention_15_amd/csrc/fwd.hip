@@ -306,9 +306,15 @@ __device__ __forceinline__ void attn_fwd_body(const FwdParams &p) {
         }
 
         // ---- online softmax ----
-        float mt = fmaxf(t[0], t[1]);
+        // Row max and sum as 4-way trees: short dependency chains.
+        float mx[4];
 #pragma unroll
-        for (int j = 2; j < 32; j += 2) mt = fmaxf(mt, fmaxf(t[j], t[j + 1]));
+        for (int k = 0; k < 4; ++k) mx[k] = fmaxf(t[k], t[k + 4]);
+#pragma unroll
+        for (int i = 8; i < 32; i += 4)
+#pragma unroll
+            for (int k = 0; k < 4; ++k) mx[k] = fmaxf(mx[k], t[i + k]);
+        float mt = fmaxf(fmaxf(mx[0], mx[1]), fmaxf(mx[2], mx[3]));
         mt = fmaxf(mt, wave_swap_halves(mt, half));
         if constexpr (!SOFTCAP) mt *= p.scale_log2;
         // Rescale O and l only when some valid row's max grew by more than
@@ -326,16 +332,16 @@ __device__ __forceinline__ void attn_fwd_body(const FwdParams &p) {
             m_run = m_new;
         }
         const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
-        float psum = 0.f;
+        float ps[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int j = 0; j < 32; ++j) {
             if constexpr (SOFTCAP)
                 t[j] = __builtin_amdgcn_exp2f(t[j] - m_use);
             else
                 t[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(t[j], p.scale_log2, -m_use));
-            psum += t[j];
+            ps[j & 3] += t[j];
         }
-        l_run += psum;
+        l_run += (ps[0] + ps[1]) + (ps[2] + ps[3]);
 
         // ---- O^T += V^T P^T ----
         u32x4_t pk[4];
