@@ -3,18 +3,21 @@
 //
 // A single query row gives too little parallelism if each (b, head) is one
 // workgroup, so the valid keys are cut into chunks and every
-// (b, KV head, chunk) becomes a workgroup that computes a partial online
-// softmax -- local max m_c, local sum l_c and the unnormalised output -- for
-// all query heads of the GQA group at once, so the group's K/V bytes are
-// read once.  A second kernel merges the partials of each (b, query head) by
-// rescaling them with exp(m_c - max m) (aegloslab "3.7 어텐션 II", sections
-// 3.7.4 and 3.7.5).
+// (b, KV head, chunk) becomes a workgroup that computes a partial softmax --
+// local max m_c, local sum l_c and the unnormalised output -- for all query
+// heads of the GQA group at once, so the group's K/V bytes are read once.  A
+// second kernel merges the partials of each (b, query head) by rescaling
+// them with exp(m_c - max m) (aegloslab "3.7 어텐션 II", sections 3.7.4 and
+// 3.7.5).
 //
 // The split kernel is bound by HBM: K and V of the chunk are streamed once
-// with 16-byte loads.  Scores use bf16 MFMA (v_mfma_f32_16x16x32_bf16, the
-// group's queries as the A operand, 16 keys per instruction as the B
-// operand), probabilities stay fp32, and P.V runs on the vector ALU with the
-// V row chunk each lane loaded.
+// with 16-byte loads.  Each wave owns a slice of the chunk (128 keys) and
+// streams it on its own (no workgroup barrier until the final merge): first
+// K, with several 16-key groups in flight, scoring the group's queries with
+// bf16 MFMA (v_mfma_f32_16x16x32_bf16: queries as the A operand, 16 keys as
+// the B operand); then the slice's softmax; then V, whose first loads are
+// already in flight, accumulating P.V in fp32 on the vector ALU.  The wave
+// partials are merged through LDS at the end.
 #include "common.h"
 
 namespace exattn {
@@ -25,6 +28,8 @@ typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr float LN2_D = 0.6931471805599453f;
 constexpr int MAX_CHUNK = 2048;
+constexpr int K_AHEAD = 3; // 16-key K groups in flight per wave
+constexpr int V_AHEAD = 8; // V row loads in flight per lane
 
 __device__ __forceinline__ float bf16lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
 __device__ __forceinline__ float bf16hi(uint32_t w) { return __builtin_bit_cast(float, w & 0xFFFF0000u); }
@@ -40,133 +45,206 @@ __device__ __forceinline__ float wave_sum(float x) {
     return x;
 }
 
-// G: query heads per KV head, rounded up to a supported size (<= 16).
-// Scores live in LDS as sc[key * GP + q], GP = max(G, 4).
-template <int D, int G>
-__global__ __launch_bounds__(256) void k_decode_split(DecodeParams p, int group) {
-    constexpr int GP = G < 4 ? 4 : G;
-    constexpr int KS = D / 32;     // k-steps of the 16x16x32 score MFMA
-    constexpr int CH = D / 8;      // 16-byte chunks per row
-    constexpr int KPI = 64 / CH;   // keys covered by one wave-wide load
-    extern __shared__ __attribute__((aligned(16))) float sm[];
-    float *sc = sm; // [chunk][GP]; reused for the wave sums after P.V
-    __shared__ float s_m[GP], s_l[GP];
+// Work items are the valid (b, KV head, chunk) triples, enumerated batch row
+// by batch row, chunk fastest.  Workgroup i takes item i, so the valid items
+// occupy the first workgroup ids.  Consecutive ids go to different XCDs
+// (round-robin dispatch), so each XCD gets an equal share of the KV bytes
+// whatever the mix of lengths; a grid indexed directly by (chunk, head, b)
+// would give the low XCDs up to one extra chunk per (b, head).  Returns false
+// for the ids past the last item.  Wave-uniform; lens is scanned 64 rows at a
+// time with a wave prefix sum.
+__device__ __forceinline__ bool decode_item(const DecodeParams &p, int &b, int &g, int &c) {
+    int i = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
+    const int lane = threadIdx.x & 63;
+    for (int b0 = 0; b0 < p.B; b0 += 64) {
+        const int bb = b0 + lane;
+        int nc = 0;
+        if (bb < p.B) {
+            int len = p.lens[bb];
+            len = len < 0 ? 0 : (len > p.T ? p.T : len);
+            nc = (len + p.chunk - 1) / p.chunk;
+        }
+        const int items = nc * p.Hkv;
+        int incl = items;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const int t = __shfl_up(incl, o);
+            if (lane >= o) incl += t;
+        }
+        const int total = __shfl(incl, 63);
+        if (i < total) {
+            const int l = __ffsll((unsigned long long)__ballot(incl > i)) - 1;
+            const int j = i - __shfl(incl - items, l);
+            const int ncl = __shfl(nc, l);
+            b = __builtin_amdgcn_readfirstlane(b0 + l);
+            g = __builtin_amdgcn_readfirstlane(j / ncl);
+            c = __builtin_amdgcn_readfirstlane(j % ncl);
+            return true;
+        }
+        i -= total;
+    }
+    return false;
+}
 
-    const int c = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+// G: query heads per KV head, rounded up to a supported size (<= 16).
+// Scores live in LDS per wave, key-major: sc[key * GP + q], GP = max(G, 4).
+template <int D, int G>
+__global__ __launch_bounds__(512) void k_decode_split(DecodeParams p, int group) {
+    constexpr int GP = G < 4 ? 4 : G;
+    constexpr int KS = D / 32;   // k-steps of the 16x16x32 score MFMA
+    constexpr int CH = D / 8;    // 16-byte chunks per row
+    constexpr int KPI = 64 / CH; // keys covered by one wave-wide V load
+    extern __shared__ __attribute__((aligned(16))) float sm[];
+
+    int b, g, c;
+    if (!decode_item(p, b, g, c)) return;
     int len = p.lens[b];
     len = len < 0 ? 0 : (len > p.T ? p.T : len);
     const int k0 = c * p.chunk;
-    if (k0 >= len) return;
     const int nk = min(p.chunk, len - k0);
 
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    const uint16_t *kbase = p.k + b * p.k_sb + g * p.k_sh + int64_t(k0) * p.k_sn;
-    const uint16_t *vbase = p.v + b * p.v_sb + g * p.v_sh + int64_t(k0) * p.v_sn;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int nwaves = blockDim.x >> 6;
+    const int cw = p.chunk / nwaves;                    // keys per wave slice (multiple of 16)
+    const int wk0 = wave * cw;                          // slice start inside the chunk
+    const int nkw = max(0, min(cw, nk - wk0));          // keys in this wave's slice
+    float *sc = sm + size_t(wave) * cw * GP;            // this wave's scores
+    const uint16_t *kbase = p.k + b * p.k_sb + g * p.k_sh + int64_t(k0 + wk0) * p.k_sn;
+    const uint16_t *vbase = p.v + b * p.v_sb + g * p.v_sh + int64_t(k0 + wk0) * p.v_sn;
 
-    // ---- scores: S = Q K^T, 16 keys per MFMA ----
-    // A operand: lane l holds query row l%16 (zero beyond the group), and for
-    // k-step s the 8 elements [(D/4)*(l/16) + 8s, +8).  B operand: lane l
-    // holds key l%16 of the 16-key group with the same element ranges, so
-    // each lane reads D/2 contiguous bytes of one K row.
-    const int r16 = lane & 15, g4 = lane >> 4;
-    bf16x8_t qa[KS];
-    {
-        const bool ok = r16 < group;
-        const uint16_t *qrow = p.q + b * p.q_sb + int64_t(g * group + (ok ? r16 : 0)) * p.q_sh;
-#pragma unroll
-        for (int s = 0; s < KS; ++s) {
-            u32x4_t x = {0u, 0u, 0u, 0u};
-            if (ok) x = *reinterpret_cast<const u32x4_t *>(qrow + (D / 4) * g4 + 8 * s);
-            qa[s] = __builtin_bit_cast(bf16x8_t, x);
-        }
-    }
-    const int ngroups = (nk + 15) >> 4;
-    constexpr int UNR = 4;
-    for (int kg0 = wave * UNR; kg0 < ngroups; kg0 += 4 * UNR) {
-        u32x4_t kb[UNR][KS];
-#pragma unroll
-        for (int u = 0; u < UNR; ++u) {
-            const int key = (kg0 + u) * 16 + r16;
-            const bool ok = (kg0 + u) < ngroups && key < nk;
-#pragma unroll
-            for (int s = 0; s < KS; ++s) {
-                u32x4_t x = {0u, 0u, 0u, 0u};
-                if (ok) x = *reinterpret_cast<const u32x4_t *>(kbase + int64_t(key) * p.k_sn + (D / 4) * g4 + 8 * s);
-                kb[u][s] = x;
-            }
-        }
-#pragma unroll
-        for (int u = 0; u < UNR; ++u) {
-            if (kg0 + u >= ngroups) break;
-            f32x4_t acc = f32x4_t{};
-#pragma unroll
-            for (int s = 0; s < KS; ++s)
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[s], __builtin_bit_cast(bf16x8_t, kb[u][s]), acc, 0, 0, 0);
-            // Lane l holds rows (queries) 4*(l/16)+r of column (key) l%16.
-            const int key = (kg0 + u) * 16 + r16;
-            if (key < nk) {
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int q = 4 * g4 + r;
-                    if (q < GP) sc[key * GP + q] = acc[r] * p.scale_log2;
-                }
-            }
-        }
-    }
-    __syncthreads();
-
-    // ---- chunk-local softmax: one wave per query ----
-    for (int q = wave; q < group; q += 4) {
-        float m = -INFINITY;
-        for (int j = lane; j < nk; j += 64) m = fmaxf(m, sc[j * GP + q]);
-        m = wave_max(m);
-        float l = 0.f;
-        for (int j = lane; j < nk; j += 64) {
-            const float e = __builtin_amdgcn_exp2f(sc[j * GP + q] - m);
-            sc[j * GP + q] = e;
-            l += e;
-        }
-        l = wave_sum(l);
-        if (lane == 0) {
-            s_m[q] = m;
-            s_l[q] = l;
-        }
-    }
-    __syncthreads();
-
-    // ---- partial O = P V on the vector ALU ----
-    // Lane l covers d-chunk l%CH of key (l/CH) within each wave-wide load.
-    const int dc = lane % CH, ksub = lane / CH;
+    // Both streams keep their loads unconditional (rows past the slice are
+    // clamped to its last key and their results discarded) and their trip
+    // counts padded to the prefetch depth, so the loop bodies have a single
+    // path and the compiler can count loads in flight instead of draining.
+    float m_w[G], l_w[G];
     float acc[G][8];
 #pragma unroll
-    for (int q = 0; q < G; ++q)
+    for (int q = 0; q < G; ++q) {
+        m_w[q] = -INFINITY;
+        l_w[q] = 0.f;
 #pragma unroll
         for (int e = 0; e < 8; ++e) acc[q][e] = 0.f;
-    constexpr int VUNR = 4;
-    for (int j0 = wave * KPI; j0 < nk; j0 += 4 * KPI * VUNR) {
-        u32x4_t vv[VUNR];
+    }
+    const int dc = lane % CH, ksub = lane / CH;
+    if (nkw > 0) {
+        // ---- pass 1: scores S = Q K^T, 16 keys per MFMA group ----
+        // A operand: lane l holds query row l%16 (zero beyond the group), and
+        // for k-step s the 8 elements [(D/4)*(l/16) + 8s, +8).  B operand:
+        // lane l holds key l%16 of the 16-key group with the same element
+        // ranges, so each lane reads D/2 contiguous bytes of one K row.
+        const int r16 = lane & 15, g4 = lane >> 4;
+        bf16x8_t qa[KS];
+        {
+            const bool ok = r16 < group;
+            const uint16_t *qrow = p.q + b * p.q_sb + int64_t(g * group + (ok ? r16 : 0)) * p.q_sh;
 #pragma unroll
-        for (int u = 0; u < VUNR; ++u) {
-            const int key = j0 + 4 * KPI * u + ksub;
-            u32x4_t x = {0u, 0u, 0u, 0u};
-            if (key < nk) x = *reinterpret_cast<const u32x4_t *>(vbase + int64_t(key) * p.v_sn + 8 * dc);
-            vv[u] = x;
+            for (int s = 0; s < KS; ++s) {
+                const u32x4_t x = *reinterpret_cast<const u32x4_t *>(qrow + (D / 4) * g4 + 8 * s);
+                qa[s] = ok ? __builtin_bit_cast(bf16x8_t, x) : bf16x8_t{};
+            }
+        }
+        auto kload = [&](int grp, u32x4_t *dst) {
+            const int key = min(grp * 16 + r16, nkw - 1);
+            const uint16_t *src = kbase + int64_t(key) * p.k_sn + (D / 4) * g4;
+#pragma unroll
+            for (int s = 0; s < KS; ++s) dst[s] = *reinterpret_cast<const u32x4_t *>(src + 8 * s);
+        };
+        const int ngroups = (nkw + 15) >> 4;
+        const int ngroups_pad = (ngroups + K_AHEAD - 1) / K_AHEAD * K_AHEAD;
+        u32x4_t kb[K_AHEAD][KS];
+        // Issue the prologue in group order (the loop waits for the oldest
+        // group only, which requires it to be the first one issued).
+#pragma unroll
+        for (int i = 0; i < K_AHEAD; ++i) {
+            kload(i, kb[i]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        for (int grp0 = 0; grp0 < ngroups_pad; grp0 += K_AHEAD) {
+#pragma unroll
+            for (int i = 0; i < K_AHEAD; ++i) {
+                const int grp = grp0 + i;
+                f32x4_t sacc = f32x4_t{};
+#pragma unroll
+                for (int s = 0; s < KS; ++s)
+                    sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[s], __builtin_bit_cast(bf16x8_t, kb[i][s]),
+                                                                    sacc, 0, 0, 0);
+                // refill this buffer with the group K_AHEAD further on
+                kload(grp + K_AHEAD, kb[i]);
+                // Lane l holds rows (queries) 4*(l/16)+r of column (key) l%16.
+                const int key = grp * 16 + r16;
+                if (key < nkw && 4 * g4 < GP)
+                    *reinterpret_cast<f32x4_t *>(sc + key * GP + 4 * g4) = sacc * p.scale_log2;
+            }
+        }
+
+        // Start the V stream before the softmax so its latency overlaps it.
+        // Lane l covers d-chunk l%CH of key (l/CH) + KPI*i of each wave-wide load.
+        auto vload = [&](int it) {
+            const int key = min(ksub + KPI * it, nkw - 1);
+            return *reinterpret_cast<const u32x4_t *>(vbase + int64_t(key) * p.v_sn + 8 * dc);
+        };
+        u32x4_t vv[V_AHEAD];
+#pragma unroll
+        for (int i = 0; i < V_AHEAD; ++i) {
+            vv[i] = vload(i);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+
+        // ---- slice softmax: per query, max and exp over the wave's keys ----
+        // (wave-private LDS, so only the wave's own ordering matters)
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+#pragma unroll
+        for (int q = 0; q < G; ++q) {
+            float m = -INFINITY;
+            for (int j = lane; j < nkw; j += 64) m = fmaxf(m, sc[j * GP + q]);
+            m_w[q] = wave_max(m);
         }
 #pragma unroll
-        for (int u = 0; u < VUNR; ++u) {
-            const int key = j0 + 4 * KPI * u + ksub;
-            if (key < nk) {
+        for (int q = 0; q < G; ++q) {
+            float l = 0.f;
+            for (int j = lane; j < nkw; j += 64) {
+                const float e = __builtin_amdgcn_exp2f(sc[j * GP + q] - m_w[q]);
+                sc[j * GP + q] = e;
+                l += e;
+            }
+            l_w[q] = wave_sum(l);
+        }
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+
+        // ---- pass 2: partial O = P V on the vector ALU ----
+        const int nit = (nkw + KPI - 1) / KPI;
+        const int nit_pad = (nit + V_AHEAD - 1) / V_AHEAD * V_AHEAD;
+        for (int it0 = 0; it0 < nit_pad; it0 += V_AHEAD) {
+#pragma unroll
+            for (int i = 0; i < V_AHEAD; ++i) {
+                const int it = it0 + i;
+                const int key = ksub + KPI * it;
+                const bool ok = key < nkw;
+                // Unpack the row first, so that its registers are free when
+                // the refill load (V_AHEAD rows ahead) is issued into them.
                 float vf[8];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    vf[2 * e] = bf16lo(vv[u][e]);
-                    vf[2 * e + 1] = bf16hi(vv[u][e]);
+                    vf[2 * e] = bf16lo(vv[i][e]);
+                    vf[2 * e + 1] = bf16hi(vv[i][e]);
                 }
+                __builtin_amdgcn_sched_barrier(0);
+                vv[i] = vload(it + V_AHEAD);
+                const int kc = ok ? key : nkw - 1;
 #pragma unroll
-                for (int q = 0; q < G; ++q) {
-                    const float pq = sc[key * GP + q];
+                for (int q4 = 0; q4 < GP; q4 += 4) {
+                    const f32x4_t pq = *reinterpret_cast<const f32x4_t *>(sc + kc * GP + q4);
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) acc[q][e] += pq * vf[e];
+                    for (int r = 0; r < 4; ++r) {
+                        if (q4 + r < G) {
+                            const float w = ok ? pq[r] : 0.f;
+#pragma unroll
+                            for (int e = 0; e < 8; ++e) acc[q4 + r][e] += w * vf[e];
+                        }
+                    }
                 }
             }
         }
@@ -178,29 +256,56 @@ __global__ __launch_bounds__(256) void k_decode_split(DecodeParams p, int group)
         for (int q = 0; q < G; ++q)
 #pragma unroll
             for (int e = 0; e < 8; ++e) acc[q][e] += __shfl_xor(acc[q][e], o);
-    __syncthreads(); // scores are no longer needed: reuse LDS for the wave sums
-    float *red = sm;  // [4 waves][G][D]
+
+    // ---- merge the wave partials (LDS reused after the barrier) ----
+    __syncthreads();
+    float *red = sm;                       // [nwaves][G][D]
+    float *wm = sm + nwaves * G * D;       // [nwaves][G]
+    float *wl = wm + nwaves * G;           // [nwaves][G]
     if (ksub == 0) {
 #pragma unroll
         for (int q = 0; q < G; ++q)
 #pragma unroll
             for (int e = 0; e < 8; ++e) red[(wave * G + q) * D + 8 * dc + e] = acc[q][e];
     }
+    if (lane < G) {
+#pragma unroll
+        for (int q = 0; q < G; ++q)
+            if (lane == q) {
+                wm[wave * G + q] = m_w[q];
+                wl[wave * G + q] = l_w[q];
+            }
+    }
     __syncthreads();
     const int64_t part_base = (int64_t(b) * p.Hq + int64_t(g) * group) * p.nchunk + c;
-    for (int i = tid; i < group * D; i += 256) {
+    for (int i = tid; i < group * D; i += blockDim.x) {
         const int q = i / D, d = i % D;
-        const float s = red[(0 * G + q) * D + d] + red[(1 * G + q) * D + d] + red[(2 * G + q) * D + d] +
-                        red[(3 * G + q) * D + d];
-        p.part_o[(part_base + int64_t(q) * p.nchunk) * D + d] = s;
-    }
-    if (tid < group) {
-        p.part_m[part_base + int64_t(tid) * p.nchunk] = s_m[tid];
-        p.part_l[part_base + int64_t(tid) * p.nchunk] = s_l[tid];
+        float M = -INFINITY;
+        for (int w = 0; w < nwaves; ++w) M = fmaxf(M, wm[w * G + q]);
+        float o = 0.f;
+        for (int w = 0; w < nwaves; ++w) {
+            const float mw = wm[w * G + q];
+            if (mw != -INFINITY) o += __builtin_amdgcn_exp2f(mw - M) * red[(w * G + q) * D + d];
+        }
+        p.part_o[(part_base + int64_t(q) * p.nchunk) * D + d] = o;
+        if (d == 0) {
+            float L = 0.f;
+            for (int w = 0; w < nwaves; ++w) {
+                const float mw = wm[w * G + q];
+                if (mw != -INFINITY) L += __builtin_amdgcn_exp2f(mw - M) * wl[w * G + q];
+            }
+            p.part_m[part_base + int64_t(q) * p.nchunk] = M;
+            p.part_l[part_base + int64_t(q) * p.nchunk] = L;
+        }
     }
 }
 
 // One workgroup of D threads per (query head, b): merge the chunk partials.
+// The chunks are read in batches of COMBINE_BATCH whose loads are all issued
+// before any is used (rows past the last chunk are clamped and weighted 0),
+// and the running max / sum / output are rescaled once per batch, so a
+// (b, head) with up to COMBINE_BATCH chunks costs one round trip to memory.
+constexpr int COMBINE_BATCH = 32;
 template <int D>
 __global__ __launch_bounds__(D) void k_decode_combine(DecodeParams p) {
     const int h = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
@@ -209,13 +314,31 @@ __global__ __launch_bounds__(D) void k_decode_combine(DecodeParams p) {
     const int nch = (len + p.chunk - 1) / p.chunk;
     const int64_t base = (int64_t(b) * p.Hq + h) * p.nchunk;
     uint16_t *orow = p.o + b * p.o_sb + h * p.o_sh;
-    float M = -INFINITY;
-    for (int c = 0; c < nch; ++c) M = fmaxf(M, p.part_m[base + c]);
-    float L = 0.f, acc = 0.f;
-    for (int c = 0; c < nch; ++c) {
-        const float w = __builtin_amdgcn_exp2f(p.part_m[base + c] - M);
-        L += w * p.part_l[base + c];
-        acc += w * p.part_o[(base + c) * D + d];
+    float M = -INFINITY, L = 0.f, acc = 0.f;
+    for (int c0 = 0; c0 < nch; c0 += COMBINE_BATCH) {
+        float mv[COMBINE_BATCH], lv[COMBINE_BATCH], ov[COMBINE_BATCH];
+#pragma unroll
+        for (int j = 0; j < COMBINE_BATCH; ++j) {
+            const int c = min(c0 + j, nch - 1);
+            mv[j] = p.part_m[base + c];
+            lv[j] = p.part_l[base + c];
+            ov[j] = p.part_o[(base + c) * D + d];
+        }
+        float Mb = M;
+#pragma unroll
+        for (int j = 0; j < COMBINE_BATCH; ++j)
+            if (c0 + j < nch) Mb = fmaxf(Mb, mv[j]);
+        // a chunk holds at least one key, so Mb is finite unless scores overflowed
+        const float r = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(M - Mb);
+        L *= r;
+        acc *= r;
+#pragma unroll
+        for (int j = 0; j < COMBINE_BATCH; ++j) {
+            const float w = c0 + j < nch ? __builtin_amdgcn_exp2f(mv[j] - Mb) : 0.f;
+            L += w * lv[j];
+            acc += w * ov[j];
+        }
+        M = Mb;
     }
     const float o = L > 0.f ? acc / L : 0.f;
     __bf16 ob = (__bf16)o;
@@ -224,15 +347,28 @@ __global__ __launch_bounds__(D) void k_decode_combine(DecodeParams p) {
         p.lse[int64_t(b) * p.Hq + h] = L > 0.f ? (M + __builtin_amdgcn_logf(L)) * LN2_D : -INFINITY;
 }
 
+// Waves per split workgroup: about one per DECODE_WAVE_KEYS keys of the
+// chunk, a power of two in [1, 8] that leaves a multiple of 16 keys per wave
+// (chunk is a multiple of 64, so 1, 2 and 4 always do).
+constexpr int DECODE_WAVE_KEYS = 128;
+static int decode_waves(int chunk) {
+    int n = 1;
+    while (n < 8 && 2 * n * DECODE_WAVE_KEYS <= chunk) n *= 2;
+    if (n == 8 && chunk % 128) n = 4;
+    return n;
+}
+
 template <int D, int G> static hipError_t launch_split(const DecodeParams &p, int group, hipStream_t stream) {
     constexpr int GP = G < 4 ? 4 : G;
-    size_t lds_scores = size_t(p.chunk) * GP * sizeof(float);
-    size_t lds_red = size_t(4) * G * D * sizeof(float);
-    size_t lds = lds_scores > lds_red ? lds_scores : lds_red;
+    const int nwaves = decode_waves(p.chunk);
+    const size_t lds_scores = size_t(p.chunk) * GP * sizeof(float);
+    const size_t lds_merge = (size_t(nwaves) * G * D + 2 * size_t(nwaves) * G) * sizeof(float);
+    const size_t lds = lds_scores > lds_merge ? lds_scores : lds_merge;
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&k_decode_split<D, G>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((k_decode_split<D, G>), dim3(p.nchunk, p.Hkv, p.B), dim3(256), lds, stream, p, group);
+    hipLaunchKernelGGL((k_decode_split<D, G>), dim3(p.nchunk, p.Hkv, p.B), dim3(64 * nwaves), lds, stream, p,
+                       group);
     return hipGetLastError();
 }
 
@@ -253,6 +389,7 @@ hipError_t launch_decode(const DecodeParams &p, int d, hipStream_t stream) {
     return d == 128 ? launch_decode_d<128>(p, stream) : launch_decode_d<64>(p, stream);
 }
 
-static_assert(MAX_CHUNK * 16 * 4 + 2 * 16 * 4 <= 160 * 1024, "decode scores and row stats must fit in LDS");
+static_assert(MAX_CHUNK * 16 * 4 <= 160 * 1024, "decode scores must fit in LDS");
+static_assert((8 * 16 * 128 + 2 * 8 * 16) * 4 <= 160 * 1024, "decode merge buffers must fit in LDS");
 
 } // namespace exattn
