@@ -239,13 +239,19 @@ __device__ __forceinline__ void attn_fwd_body(const FwdParams &p) {
     // streams into the other buffer.  The loop below is unrolled by two and
     // the lambda is inlined with stage = 0 and 1, so every LDS address folds
     // into a per-lane register plus an immediate offset.
+    // Tile-list entries are read one iteration before they are needed: the
+    // entry of tile it+1 was loaded during iteration it-1 and has arrived by
+    // the end-of-iteration wait, so no list read is ever waited on alone.
+    int ent_cur = 0, ent_next_v = 0;
     auto step = [&](int it, const int stage) {
-        const int ent = __builtin_amdgcn_readfirstlane(tiles[it]);
+        const int ent = ent_cur;
         const int kt = ent >> 1;
         const bool partial = ent & TILE_PARTIAL;
+        const int ent_next = __builtin_amdgcn_readfirstlane(ent_next_v);
+        const int ent_next2_v = tiles[min(it + 2, ntiles - 1)];
         // The other buffer was last read in iteration it-1, which every wave
         // has finished (barrier at the end of it), so it can be refilled now.
-        if (it + 1 < ntiles) issue_tile(__builtin_amdgcn_readfirstlane(tiles[it + 1]) >> 1, 1 - stage);
+        if (it + 1 < ntiles) issue_tile(ent_next >> 1, 1 - stage);
 
         const lds_u8 *ks = smem + stage * C::STAGE_BYTES;
         const lds_u8 *vs = ks + C::TILE_BYTES;
@@ -388,9 +394,15 @@ __device__ __forceinline__ void attn_fwd_body(const FwdParams &p) {
         // this tile's buffer must be free before it is refilled.
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
+        ent_cur = ent_next;
+        ent_next_v = ent_next2_v;
     };
 
-    if (ntiles > 0) issue_tile(__builtin_amdgcn_readfirstlane(tiles[0]) >> 1, 0);
+    if (ntiles > 0) {
+        ent_cur = __builtin_amdgcn_readfirstlane(tiles[0]);
+        issue_tile(ent_cur >> 1, 0);
+        ent_next_v = tiles[min(1, ntiles - 1)];
+    }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     for (int it = 0; it < ntiles; it += 2) {
