@@ -113,8 +113,12 @@ __device__ __forceinline__ void attn_fwd_body(const FwdParams &p) {
     using C = FwdCfg<D>;
     lds_u8 *smem = (lds_u8 *)(smem_raw); // generic -> LDS address space
 
-    const int tid = threadIdx.x;
-    const int wave = tid >> 6, lane = tid & 63;
+    // Builtins rather than threadIdx/blockIdx: the latter may be lowered to
+    // device-library calls.  The wave index is made a scalar so that all
+    // per-wave addresses (LDS destinations of the tile loads) are SGPRs.
+    const int tid = __builtin_amdgcn_workitem_id_x();
+    const int bid = __builtin_amdgcn_workgroup_id_x();
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int col = lane & 31, half = lane >> 5;
 
     // Work assignment.  A "group" is everything that reads the same K/V:
@@ -128,12 +132,12 @@ __device__ __forceinline__ void attn_fwd_body(const FwdParams &p) {
     const int ngroups = p.B * p.Hkv;
     int group, within;
     if ((ngroups & 7) == 0) {
-        const int x = blockIdx.x & 7, j = blockIdx.x >> 3;
+        const int x = bid & 7, j = bid >> 3;
         group = x + 8 * (j / per_group);
         within = j % per_group;
     } else {
-        group = blockIdx.x / per_group;
-        within = blockIdx.x % per_group;
+        group = bid / per_group;
+        within = bid % per_group;
     }
     const int b = group / p.Hkv, hk = group % p.Hkv;
     // Values read from memory are not known to be wave-uniform; readfirstlane
@@ -171,14 +175,16 @@ __device__ __forceinline__ void attn_fwd_body(const FwdParams &p) {
     // Wave w, load u fills LDS bytes [(LOADS*w + u) KiB, +1 KiB) of a tile:
     // row ROWS_PER_LOAD*(LOADS*w + u) + lane/CHUNKS, physical chunk
     // lane%CHUNKS, which holds logical chunk (lane%CHUNKS) ^ swz(row).  The
-    // per-lane element offsets inside a tile fit 32 bits (stride_n < 2^24).
+    // per-lane byte offsets inside a tile fit 32 bits (stride_n < 2^24).
     auto ld_row = [&](int u) { return C::ROWS_PER_LOAD * (C::LOADS * wave + u) + lane / C::CHUNKS; };
     auto ld_col = [&](int u) { return 8u * uint32_t((lane % C::CHUNKS) ^ swz<D>(ld_row(u))); };
+    // Byte offsets, so that each load is a scalar base plus a 32-bit
+    // per-lane offset (the saddr + voffset form: no 64-bit VALU adds).
     uint32_t ld_koff[C::LOADS], ld_voff[C::LOADS];
 #pragma unroll
     for (int u = 0; u < C::LOADS; ++u) {
-        ld_koff[u] = uint32_t(ld_row(u)) * uint32_t(p.k_sn) + ld_col(u);
-        ld_voff[u] = uint32_t(ld_row(u)) * uint32_t(p.v_sn) + ld_col(u);
+        ld_koff[u] = 2u * (uint32_t(ld_row(u)) * uint32_t(p.k_sn) + ld_col(u));
+        ld_voff[u] = 2u * (uint32_t(ld_row(u)) * uint32_t(p.v_sn) + ld_col(u));
     }
     auto issue_tile = [&](int kt, const int stage) {
         const int key0 = kt * BLOCK_N;
@@ -189,8 +195,10 @@ __device__ __forceinline__ void attn_fwd_body(const FwdParams &p) {
         if (key0 + BLOCK_N <= p.N) {
 #pragma unroll
             for (int u = 0; u < C::LOADS; ++u) {
-                __builtin_amdgcn_global_load_lds(kt_base + ld_koff[u], kdst + u * 1024, 16, 0, 0);
-                __builtin_amdgcn_global_load_lds(vt_base + ld_voff[u], vdst + u * 1024, 16, 0, 0);
+                __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint8_t *>(kt_base) + ld_koff[u],
+                                                 kdst + u * 1024, 16, 0, 0);
+                __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint8_t *>(vt_base) + ld_voff[u],
+                                                 vdst + u * 1024, 16, 0, 0);
             }
         } else {
             const int last = p.N - 1 - key0; // rows past N re-read row N-1 (always masked)
