@@ -14,13 +14,10 @@
 
 namespace exattn {
 
-// One thread per (b, i): the visible interval of query row i.
-__global__ void k_mask_rows(attn_mask_spec spec, int B, int N, int32_t *lo_out,
-                            int32_t *hi_out) {
-    const int64_t idx = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
-    if (idx >= int64_t(B) * N) return;
-    const int b = int(idx / N);
-    const int i = int(idx % N);
+// The visible interval [lo, hi] of query row i of batch row b (lo > hi when
+// no key is visible: then lo = 1, hi = 0).
+__device__ __forceinline__ void row_interval(const attn_mask_spec &spec, int b, int N, int i, int &lo_out,
+                                             int &hi_out) {
     int64_t lo = 0, hi = int64_t(N) - 1;
     if (spec.flags & ATTN_MASK_CAUSAL) hi = min(hi, int64_t(i));
     if (spec.flags & ATTN_MASK_WINDOW) {
@@ -45,73 +42,79 @@ __global__ void k_mask_rows(attn_mask_spec spec, int B, int N, int32_t *lo_out,
         lo = max(lo, start);
         hi = min(hi, end - 1);
     }
-    if (lo > hi) { lo = 1; hi = 0; } // empty row
-    lo_out[idx] = int32_t(lo);
-    hi_out[idx] = int32_t(hi);
+    if (lo > hi) { lo = 1; hi = 0; }
+    lo_out = int(lo);
+    hi_out = int(hi);
 }
 
-// One workgroup per (query tile, b).  Thread t classifies a contiguous run of
-// key tiles; a block-wide prefix sum then writes the visited tiles in order.
-__global__ __launch_bounds__(256) void k_mask_tiles(uint32_t flags, int N, int nqt, int nkt,
-                                                    const int32_t *lo_in, const int32_t *hi_in,
-                                                    int32_t *count_out, int32_t *list_out) {
+// One workgroup (4 waves) per (query tile, b).  Threads 0..127 compute and
+// store the intervals of the tile's rows.  Then, 256 key tiles at a time,
+// wave w classifies key tiles w*64 + j (j = 0..63) one after another: every
+// lane tests two of the 128 rows and two ballots give "any row sees a key"
+// and "every row sees every key"; lane j keeps tile j's result.  The visited
+// tiles are then written in key order with a ballot/popcount compaction.
+__global__ __launch_bounds__(256) void k_mask_tiles(attn_mask_spec spec, int N, int nqt, int nkt,
+                                                    int32_t *lo_out, int32_t *hi_out, int32_t *count_out,
+                                                    int32_t *list_out) {
     __shared__ int32_t s_lo[BLOCK_M], s_hi[BLOCK_M];
-    __shared__ int32_t s_valid[BLOCK_M];
-    __shared__ int32_t s_cnt[256];
+    __shared__ int32_t s_wcnt[4];
     const int qt = blockIdx.x, b = blockIdx.y, t = threadIdx.x;
+    const int lane = t & 63, w = t >> 6;
     const int r0 = qt * BLOCK_M;
     if (t < BLOCK_M) {
+        int lo = 1, hi = 0;
         const int row = r0 + t;
-        const bool ok = row < N;
-        s_valid[t] = ok;
-        s_lo[t] = ok ? lo_in[int64_t(b) * N + row] : 1;
-        s_hi[t] = ok ? hi_in[int64_t(b) * N + row] : 0;
-    }
-    __syncthreads();
-    const bool no_skip = flags & ATTN_MASK_NO_SKIP;
-    const int per = (nkt + 255) / 256;
-    const int kt0 = min(nkt, t * per), kt1 = min(nkt, kt0 + per);
-    // Count this thread's visited tiles; the classification is repeated in
-    // the write pass below (it is cheap) instead of being stored.
-    int n_mine = 0;
-    for (int kt = kt0; kt < kt1; ++kt) {
-        const int c0 = kt * BLOCK_N, c1 = c0 + BLOCK_N - 1;
-        bool any = false, full = true;
-        for (int r = 0; r < BLOCK_M; ++r) {
-            if (!s_valid[r]) continue;
-            const int lo = s_lo[r], hi = s_hi[r];
-            if (max(lo, c0) <= min(hi, c1)) any = true;
-            if (!(lo <= c0 && hi >= c1)) full = false;
+        if (row < N) {
+            row_interval(spec, b, N, row, lo, hi);
+            lo_out[int64_t(b) * N + row] = lo;
+            hi_out[int64_t(b) * N + row] = hi;
         }
-        if (no_skip) { any = true; full = false; }
-        n_mine += any;
+        s_lo[t] = lo;
+        s_hi[t] = hi;
     }
-    s_cnt[t] = n_mine;
     __syncthreads();
-    // Exclusive prefix over 256 counts (Hillis-Steele in shared memory).
-    for (int s = 1; s < 256; s <<= 1) {
-        int add = t >= s ? s_cnt[t - s] : 0;
-        __syncthreads();
-        s_cnt[t] += add;
-        __syncthreads();
-    }
-    const int base = s_cnt[t] - n_mine;
+    // Rows past N are ignored; a row with no visible key (lo > hi) makes
+    // every tile PARTIAL but no tile visited.
+    const bool oka = r0 + lane < N, okb = r0 + lane + 64 < N;
+    const int lo_a = s_lo[lane], hi_a = s_hi[lane];
+    const int lo_b = s_lo[lane + 64], hi_b = s_hi[lane + 64];
+    const bool no_skip = spec.flags & ATTN_MASK_NO_SKIP;
     const int64_t item = int64_t(b) * nqt + qt;
     int32_t *list = list_out + item * nkt;
-    int w = base;
-    for (int kt = kt0; kt < kt1; ++kt) {
-        const int c0 = kt * BLOCK_N, c1 = c0 + BLOCK_N - 1;
-        bool any = false, full = true;
-        for (int r = 0; r < BLOCK_M; ++r) {
-            if (!s_valid[r]) continue;
-            const int lo = s_lo[r], hi = s_hi[r];
-            if (max(lo, c0) <= min(hi, c1)) any = true;
-            if (!(lo <= c0 && hi >= c1)) full = false;
+    int base = 0;
+    for (int k0 = 0; k0 < nkt; k0 += 256) {
+        bool my_any = false, my_full = false;
+        const int kw = k0 + w * 64;
+        for (int j = 0; j < 64; ++j) {
+            const int kt = kw + j;
+            if (kt >= nkt) break; // wave-uniform
+            const int c0 = kt * BLOCK_N, c1 = c0 + BLOCK_N - 1;
+            const bool seen = (oka && max(lo_a, c0) <= min(hi_a, c1)) || (okb && max(lo_b, c0) <= min(hi_b, c1));
+            const bool gap = (oka && !(lo_a <= c0 && hi_a >= c1)) || (okb && !(lo_b <= c0 && hi_b >= c1));
+            bool any = __any(seen), full = !__any(gap);
+            if (no_skip) {
+                any = true;
+                full = false;
+            }
+            if (lane == j) {
+                my_any = any;
+                my_full = full;
+            }
         }
-        if (no_skip) { any = true; full = false; }
-        if (any) list[w++] = (kt << 1) | (full ? 0 : TILE_PARTIAL);
+        const uint64_t vis = __ballot(my_any);
+        if (lane == 0) s_wcnt[w] = __popcll(vis);
+        __syncthreads();
+        int woff = base;
+        for (int x = 0; x < w; ++x) woff += s_wcnt[x];
+        const int total = s_wcnt[0] + s_wcnt[1] + s_wcnt[2] + s_wcnt[3];
+        if (my_any) {
+            const int pos = woff + __popcll(vis & ((uint64_t(1) << lane) - 1));
+            list[pos] = ((kw + lane) << 1) | (my_full ? 0 : TILE_PARTIAL);
+        }
+        base += total;
+        __syncthreads(); // s_wcnt is rewritten by the next round
     }
-    if (t == 255) count_out[item] = s_cnt[255];
+    if (t == 0) count_out[item] = base;
 }
 
 // One workgroup per batch row: order[b][rank] = query tile, ranked by
@@ -140,15 +143,9 @@ hipError_t launch_mask_build(const attn_mask_spec &spec, const MaskLayout &L, vo
     int32_t *cnt = reinterpret_cast<int32_t *>(base + L.off_count);
     int32_t *list = reinterpret_cast<int32_t *>(base + L.off_list);
     int32_t *order = reinterpret_cast<int32_t *>(base + L.off_order);
-    const int64_t rows = int64_t(L.B) * L.N;
-    const int64_t nblk = (rows + 255) / 256;
-    hipLaunchKernelGGL(k_mask_rows, dim3(unsigned(nblk)), dim3(256), 0, stream, spec, L.B, L.N,
-                       lo, hi);
+    hipLaunchKernelGGL(k_mask_tiles, dim3(L.nqt, L.B), dim3(256), 0, stream, spec, L.N, L.nqt, L.nkt, lo, hi,
+                       cnt, list);
     hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k_mask_tiles, dim3(L.nqt, L.B), dim3(256), 0, stream, spec.flags, L.N,
-                       L.nqt, L.nkt, lo, hi, cnt, list);
-    e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(k_mask_order, dim3(L.B), dim3(1024), 0, stream, L.nqt, cnt, order);
     return hipGetLastError();
