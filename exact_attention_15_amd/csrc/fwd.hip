@@ -104,6 +104,37 @@ __device__ __forceinline__ u32x2_t lds_read_tr16(const lds_u8 *base, int off) {
     return __builtin_bit_cast(u32x2_t, v);
 }
 
+// HBM -> LDS DMA: lane l writes `bytes` bytes at LDS address m0 + bytes*l.
+// Issued through inline assembly so that the compiler does not take later
+// LDS reads as dependent on it: it cannot tell the two tile buffers apart
+// and would wait for every DMA in flight before the V transpose reads,
+// halving the time a tile load has to arrive.  The kernel orders these
+// writes itself (s_waitcnt vmcnt, then a workgroup barrier, before a buffer
+// is read).  One wait state separates the M0 write from the DMA.
+__device__ __forceinline__ void dma16_saddr(const void *base, uint32_t voff, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+                 :
+                 : "s"(lds), "v"(voff), "s"(base)
+                 : "memory", "m0");
+}
+__device__ __forceinline__ void dma16(const void *addr, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+                 :
+                 : "s"(lds), "v"(addr)
+                 : "memory", "m0");
+}
+// Wait until every vector-memory operation of this wave has completed.  The
+// inline-assembly wait covers the DMA above, which the compiler does not
+// see; the builtin tells the compiler's own bookkeeping that nothing is in
+// flight any more, so it adds no waits of its own later.
+__device__ __forceinline__ void wait_vmem_all() {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0x0F70); // vmcnt(0), expcnt and lgkmcnt unconstrained
+}
+__device__ __forceinline__ uint32_t lds_addr(const __attribute__((address_space(3))) uint8_t *p) {
+    return uint32_t(reinterpret_cast<uintptr_t>(p));
+}
+
 extern __shared__ __attribute__((aligned(1024))) uint8_t smem_raw[];
 
 // The kernel body is a device template; the __global__ entry points below
@@ -195,20 +226,16 @@ __device__ __forceinline__ void attn_fwd_body(const FwdParams &p) {
         if (key0 + BLOCK_N <= p.N) {
 #pragma unroll
             for (int u = 0; u < C::LOADS; ++u) {
-                __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint8_t *>(kt_base) + ld_koff[u],
-                                                 kdst + u * 1024, 16, 0, 0);
-                __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint8_t *>(vt_base) + ld_voff[u],
-                                                 vdst + u * 1024, 16, 0, 0);
+                dma16_saddr(kt_base, ld_koff[u], lds_addr(kdst + u * 1024));
+                dma16_saddr(vt_base, ld_voff[u], lds_addr(vdst + u * 1024));
             }
         } else {
             const int last = p.N - 1 - key0; // rows past N re-read row N-1 (always masked)
 #pragma unroll
             for (int u = 0; u < C::LOADS; ++u) {
                 const int r = min(ld_row(u), last);
-                __builtin_amdgcn_global_load_lds(kt_base + int64_t(r) * p.k_sn + ld_col(u),
-                                                 kdst + u * 1024, 16, 0, 0);
-                __builtin_amdgcn_global_load_lds(vt_base + int64_t(r) * p.v_sn + ld_col(u),
-                                                 vdst + u * 1024, 16, 0, 0);
+                dma16(kt_base + int64_t(r) * p.k_sn + ld_col(u), lds_addr(kdst + u * 1024));
+                dma16(vt_base + int64_t(r) * p.v_sn + ld_col(u), lds_addr(vdst + u * 1024));
             }
         }
     };
@@ -400,7 +427,7 @@ __device__ __forceinline__ void attn_fwd_body(const FwdParams &p) {
 
         // The next tile's LDS writes must land before anyone reads them, and
         // this tile's buffer must be free before it is refilled.
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        wait_vmem_all();
         __syncthreads();
         ent_cur = ent_next;
         ent_next_v = ent_next2_v;
@@ -411,7 +438,7 @@ __device__ __forceinline__ void attn_fwd_body(const FwdParams &p) {
         issue_tile(ent_cur >> 1, 0);
         ent_next_v = tiles[min(1, ntiles - 1)];
     }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    wait_vmem_all();
     __syncthreads();
     for (int it = 0; it < ntiles; it += 2) {
         step(it, 0);
