@@ -184,6 +184,8 @@ attn_status attn_decode(attn_tensor q, attn_tensor k_cache, attn_tensor v_cache,
     if ((st = check_tensor(k_cache, "k_cache", true)) != ATTN_OK) return st;
     if ((st = check_tensor(v_cache, "v_cache", true)) != ATTN_OK) return st;
     if ((st = check_tensor(o, "o", false)) != ATTN_OK) return st;
+    if (k_cache.stride_n >= (int64_t(1) << 20) || v_cache.stride_n >= (int64_t(1) << 20))
+        return fail(ATTN_ERR_UNSUPPORTED, "attn_decode: k/v cache token stride must be below 2^20 elements");
     if (!lens) return fail(ATTN_ERR_INVALID, "attn_decode: null lens");
     if (!lse) return fail(ATTN_ERR_INVALID, "attn_decode: null lse");
     const int nchunk = T > 0 ? (T + chunk - 1) / chunk : 1;

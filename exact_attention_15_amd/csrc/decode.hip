@@ -25,14 +25,13 @@ namespace exattn {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
 constexpr float LN2_D = 0.6931471805599453f;
 constexpr int MAX_CHUNK = 2048;
 constexpr int K_AHEAD = 3; // 16-key K groups in flight per wave
-constexpr int V_AHEAD = 8; // V row loads in flight per lane
+constexpr int V_PAIRS = 4; // V row pairs (two 16-byte loads each) in flight per lane
 
-__device__ __forceinline__ float bf16lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
-__device__ __forceinline__ float bf16hi(uint32_t w) { return __builtin_bit_cast(float, w & 0xFFFF0000u); }
 
 __device__ __forceinline__ float wave_max(float x) {
 #pragma unroll
@@ -94,6 +93,7 @@ __global__ __launch_bounds__(512) void k_decode_split(DecodeParams p, int group)
     constexpr int KS = D / 32;   // k-steps of the 16x16x32 score MFMA
     constexpr int CH = D / 8;    // 16-byte chunks per row
     constexpr int KPI = 64 / CH; // keys covered by one wave-wide V load
+    constexpr int KP = 2 * KPI;  // keys per V iteration (each lane takes a pair)
     extern __shared__ __attribute__((aligned(16))) float sm[];
 
     int b, g, c;
@@ -179,15 +179,21 @@ __global__ __launch_bounds__(512) void k_decode_split(DecodeParams p, int group)
         }
 
         // Start the V stream before the softmax so its latency overlaps it.
-        // Lane l covers d-chunk l%CH of key (l/CH) + KPI*i of each wave-wide load.
-        auto vload = [&](int it) {
-            const int key = min(ksub + KPI * it, nkw - 1);
-            return *reinterpret_cast<const u32x4_t *>(vbase + int64_t(key) * p.v_sn + 8 * dc);
+        // Lane l covers d-chunk l%CH of the key pair 2*(l/CH) + KP*it and
+        // the key after it (KP keys per wave per iteration, two row loads).
+        // Rows are addressed with 32-bit byte offsets from the slice base:
+        // key < 2048 and the token stride is below 2^20 elements.
+        const uint8_t *vb8 = reinterpret_cast<const uint8_t *>(vbase);
+        const uint32_t vrow = 2u * uint32_t(p.v_sn), vcol = 16u * uint32_t(dc);
+        auto vload2 = [&](int it, u32x4_t &xa, u32x4_t &xb) {
+            const int ka = 2 * ksub + KP * it;
+            xa = *reinterpret_cast<const u32x4_t *>(vb8 + (__umul24(uint32_t(min(ka, nkw - 1)), vrow) + vcol));
+            xb = *reinterpret_cast<const u32x4_t *>(vb8 + (__umul24(uint32_t(min(ka + 1, nkw - 1)), vrow) + vcol));
         };
-        u32x4_t vv[V_AHEAD];
+        u32x4_t va[V_PAIRS], vb[V_PAIRS];
 #pragma unroll
-        for (int i = 0; i < V_AHEAD; ++i) {
-            vv[i] = vload(i);
+        for (int i = 0; i < V_PAIRS; ++i) {
+            vload2(i, va[i], vb[i]);
             __builtin_amdgcn_sched_barrier(0);
         }
 
@@ -211,45 +217,55 @@ __global__ __launch_bounds__(512) void k_decode_split(DecodeParams p, int group)
             }
             l_w[q] = wave_sum(l);
         }
+        // Zero the probabilities of the padding keys the V loop runs over,
+        // [nkw, round up to KP * V_PAIRS), which stay inside the slice (its
+        // length is a multiple of that), so the loop needs no key checks.
+        const int nkw_pad = (nkw + KP * V_PAIRS - 1) / (KP * V_PAIRS) * (KP * V_PAIRS);
+        for (int j = nkw + lane; j < nkw_pad; j += 64)
+#pragma unroll
+            for (int q = 0; q < GP; ++q) sc[j * GP + q] = 0.f;
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
 
-        // ---- pass 2: partial O = P V on the vector ALU ----
-        const int nit = (nkw + KPI - 1) / KPI;
-        const int nit_pad = (nit + V_AHEAD - 1) / V_AHEAD * V_AHEAD;
-        for (int it0 = 0; it0 < nit_pad; it0 += V_AHEAD) {
+        // ---- pass 2: partial O = P V on the vector ALU, two keys at a time ----
+        // The two rows are interleaved into bf16 pairs (V[ka][e], V[kb][e])
+        // with v_perm and dotted with the matching probability pair (P
+        // rounded to bf16, as the P V product of the forward pass uses it)
+        // by v_dot2_f32_bf16, which accumulates in fp32.
+        const int nit = nkw_pad / KP;
+        for (int it0 = 0; it0 < nit; it0 += V_PAIRS) {
 #pragma unroll
-            for (int i = 0; i < V_AHEAD; ++i) {
+            for (int i = 0; i < V_PAIRS; ++i) {
                 const int it = it0 + i;
-                const int key = ksub + KPI * it;
-                const bool ok = key < nkw;
-                // Unpack the row first, so that its registers are free when
-                // the refill load (V_AHEAD rows ahead) is issued into them.
-                float vf[8];
+                const int ka = 2 * ksub + KP * it;
+                // Interleave first, so that the row registers are free when
+                // the refill loads (V_PAIRS pairs ahead) are issued into them.
+                bf16x2_t vp[8];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    vf[2 * e] = bf16lo(vv[i][e]);
-                    vf[2 * e + 1] = bf16hi(vv[i][e]);
+                for (int w = 0; w < 4; ++w) {
+                    vp[2 * w] = __builtin_bit_cast(bf16x2_t, __builtin_amdgcn_perm(vb[i][w], va[i][w], 0x05040100u));
+                    vp[2 * w + 1] = __builtin_bit_cast(bf16x2_t, __builtin_amdgcn_perm(vb[i][w], va[i][w], 0x07060302u));
                 }
                 __builtin_amdgcn_sched_barrier(0);
-                vv[i] = vload(it + V_AHEAD);
-                const int kc = ok ? key : nkw - 1;
+                vload2(it + V_PAIRS, va[i], vb[i]);
 #pragma unroll
                 for (int q4 = 0; q4 < GP; q4 += 4) {
-                    const f32x4_t pq = *reinterpret_cast<const f32x4_t *>(sc + kc * GP + q4);
+                    const f32x4_t pa = *reinterpret_cast<const f32x4_t *>(sc + ka * GP + q4);
+                    const f32x4_t pb = *reinterpret_cast<const f32x4_t *>(sc + (ka + 1) * GP + q4);
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
                         if (q4 + r < G) {
-                            const float w = ok ? pq[r] : 0.f;
+                            const bf16x2_t pp = {(__bf16)pa[r], (__bf16)pb[r]};
 #pragma unroll
-                            for (int e = 0; e < 8; ++e) acc[q4 + r][e] += w * vf[e];
+                            for (int e = 0; e < 8; ++e)
+                                acc[q4 + r][e] = __builtin_amdgcn_fdot2_f32_bf16(vp[e], pp, acc[q4 + r][e], false);
                         }
                     }
                 }
             }
         }
     }
-    // Reduce over the KPI keys of a wave-wide load (lanes with equal dc).
+    // Reduce over the lanes that share a d-chunk (equal dc).
 #pragma unroll
     for (int o = CH; o < 64; o <<= 1)
 #pragma unroll
@@ -348,13 +364,13 @@ __global__ __launch_bounds__(D) void k_decode_combine(DecodeParams p) {
 }
 
 // Waves per split workgroup: about one per DECODE_WAVE_KEYS keys of the
-// chunk, a power of two in [1, 8] that leaves a multiple of 16 keys per wave
-// (chunk is a multiple of 64, so 1, 2 and 4 always do).
+// chunk, a power of two in [1, 8] that leaves a multiple of 64 keys per wave
+// (chunk is a multiple of 64; the V loop pads a slice to 32 or 64 keys).
 constexpr int DECODE_WAVE_KEYS = 128;
 static int decode_waves(int chunk) {
     int n = 1;
     while (n < 8 && 2 * n * DECODE_WAVE_KEYS <= chunk) n *= 2;
-    if (n == 8 && chunk % 128) n = 4;
+    while ((chunk / 64) % n) n /= 2;
     return n;
 }
 

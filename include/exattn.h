@@ -144,6 +144,7 @@ attn_status attn_fwd(attn_tensor q, attn_tensor k, attn_tensor v, attn_tensor o,
  *   o [B,Hq,1,d] bf16 (stride_n unused); lse fp32 [B][Hq] contiguous
  *     (natural log; -inf and O = 0 when lens[b] == 0).
  *   chunk: keys per split, a multiple of 64 in [64, 2048].
+ *   k_cache / v_cache token strides (stride_n) must be below 2^20 elements.
  *   workspace: >= attn_decode_workspace_size(B, Hq, T, d, chunk) bytes.
  * Supported: d in {64, 128}; Hq % Hkv == 0 with Hq/Hkv <= 16.
  * Errors: ATTN_ERR_INVALID, ATTN_ERR_UNSUPPORTED, ATTN_ERR_WORKSPACE,

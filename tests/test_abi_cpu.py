@@ -113,3 +113,7 @@ def test_decode_validation_before_launch(lib):
     assert call(chunk=4096) == b.ATTN_ERR_UNSUPPORTED
     assert call(lens=None) == b.ATTN_ERR_INVALID
     assert call() == b.ATTN_ERR_WORKSPACE
+    # cache token stride at 2^20 elements: rows are addressed with 32-bit offsets
+    wide = _t(16, 0, 0, 1 << 20)
+    assert lib.attn_decode(t, wide, t, 16, t, ctypes.c_void_p(16), 2, 8, 2, 4096, 128, 1024,
+                           ctypes.c_float(0.1), None, 0, None) == b.ATTN_ERR_UNSUPPORTED
