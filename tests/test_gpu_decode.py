@@ -96,3 +96,22 @@ def test_decode_strided_cache(ea):
     o2, l2 = ea.decode(to_dev(q), Kt, Vt, lens)
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_decode_workspace_reuse(ea):
+    # One workspace serves consecutive calls with different lengths (every
+    # chunk partial a call reads is written by that call): each result equals
+    # the one computed with a fresh workspace.
+    B, Hq, Hkv, T, d, chunk = 5, 8, 2, 5000, 128, 512
+    q, kc, vc, _ = gen.decode_inputs(131, B, Hq, Hkv, T, d)
+    Q, K, V = to_dev(q), to_dev(kc), to_dev(vc)
+    ws = torch.full((ea.decode_workspace_bytes(B, Hq, T, d, chunk),), 0x7F, dtype=torch.uint8, device="cuda")
+    for lens in ([5000, 1, 0, 2049, 777], [512, 4999, 3000, 0, 1], [0, 0, 0, 0, 0], [64] * 5):
+        L = torch.tensor(lens, dtype=torch.int32, device="cuda")
+        print(f"[case] reuse lens={lens}", flush=True)
+        o1, l1 = ea.decode(Q, K, V, L, chunk=chunk, workspace=ws)
+        o2, l2 = ea.decode(Q, K, V, L, chunk=chunk)
+        torch.cuda.synchronize()
+        assert torch.equal(o1, o2) and torch.equal(l1, l2), lens
+    run_decode(ea, B=B, Hq=Hq, Hkv=Hkv, T=T, d=d, seed=131, lens=[512, 4999, 3000, 0, 1], chunk=chunk,
+               label="reuse oracle")
