@@ -48,6 +48,9 @@ def _load():
         lib.oracle_decode.restype = i32
         lib.oracle_decode.argtypes = [P, P, P, P, P, P, i32, i32, i32, i32,
                                       i32, f64, P, P]
+        lib.oracle_bwd.restype = i32
+        lib.oracle_bwd.argtypes = [P, P, P, P, P, P, P, i32, i32, i32, i32, i32,
+                                   i32, i64, i64, f64, P, i32, f64, P, P, P]
         lib.oracle_threads.restype = i32
         lib.oracle_threads.argtypes = []
         _lib = lib
@@ -125,6 +128,51 @@ def fwd(q, k, v, *, scale, causal=False, window=None, doc_offsets=None,
         if p is not None:
             p = p.reshape(B, Hq, N, N)
     return (o, lse, p) if want_probs else (o, lse)
+
+
+def bwd(q, k, v, dout, *, scale, causal=False, window=None, doc_offsets=None,
+        softcap=None):
+    """Gradients of exact attention, fp64: (dq [B,Hq,N,d], dk, dv [B,Hkv,N,d]).
+
+    q, k, v as for fwd(); dout [B,Hq,N,d] bf16 bits is the gradient of the
+    loss with respect to O.
+    """
+    lib = _load()
+    for a in (q, k, v, dout):
+        if a.dtype != np.uint16:
+            raise TypeError("oracle inputs are bf16 bit patterns (uint16)")
+    B, Hq, N, d = q.shape
+    Hkv = k.shape[1]
+    if dout.shape != q.shape:
+        raise ValueError("dout must have the shape of q")
+    flags = 0
+    wl = wr = 0
+    if causal:
+        flags |= CAUSAL
+    if window is not None:
+        flags |= WINDOW
+        wl, wr = (window, window) if np.isscalar(window) else window
+    offs = None
+    doc_stride = 0
+    if doc_offsets is not None:
+        flags |= DOCS
+        offs = np.ascontiguousarray(doc_offsets, dtype=np.int32)
+        doc_stride = offs.shape[1]
+    cap = 0.0
+    if softcap is not None:
+        flags |= SOFTCAP
+        cap = float(softcap)
+    dout = np.ascontiguousarray(dout)
+    dq = np.empty((B, Hq, N, d), dtype=np.float64)
+    dk = np.empty((B, Hkv, N, d), dtype=np.float64)
+    dv = np.empty((B, Hkv, N, d), dtype=np.float64)
+    qs, ks, vs = _strides(q), _strides(k), _strides(v)
+    rc = lib.oracle_bwd(_ptr(q), _ptr(qs), _ptr(k), _ptr(ks), _ptr(v), _ptr(vs), _ptr(dout),
+                        B, Hq, Hkv, N, d, flags, int(wl), int(wr), cap, _ptr(offs), doc_stride,
+                        float(scale), _ptr(dq), _ptr(dk), _ptr(dv))
+    if rc != 0:
+        raise ValueError("oracle_bwd rejected its arguments")
+    return dq, dk, dv
 
 
 def decode(q, kc, vc, lens, *, scale):

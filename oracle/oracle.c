@@ -258,3 +258,104 @@ int oracle_decode(const uint16_t *q, const uint16_t *kc, const int64_t *k_stride
     }
     return 0;
 }
+
+/*
+ * Backward of the forward above (gradients of a loss through O), fp64.
+ * For every query row i of (b, h), with the row's scores s (scaled, masked,
+ * soft-capped) and probabilities P recomputed from q, k, v:
+ *   dP_ij = dO_i . v_j,  D_i = sum_j P_ij dP_ij  (= dO_i . O_i),
+ *   dS_ij = P_ij (dP_ij - D_i)                   (softmax backward),
+ *   dU_ij = dS_ij * (1 - (s_ij / c)^2)           (soft cap: d c tanh(u/c) / du;
+ *                                                 dU = dS without a cap),
+ *   dq_i += scale * sum_j dU_ij k_j,
+ *   dk_j += scale * dU_ij q_i,   dv_j += P_ij dO_i,
+ * where k_j, v_j belong to KV head h / (Hq / Hkv), so the dk and dv of a KV
+ * head sum over its query heads.  These are the gradients the recomputation
+ * strategy of youngju.dev "FlashAttention 논문 분석" (section "Recomputation
+ * 전략") evaluates from the saved row statistics; here they follow from the
+ * definition directly (the chain rule through softmax and the matrix
+ * products).  Masked keys have P = 0, hence zero gradient.
+ *   dout [B][Hq][N][d] contiguous bf16 bits; outputs contiguous fp64:
+ *   out_dq [B][Hq][N][d], out_dk / out_dv [B][Hkv][N][d].
+ * Returns 0, or -1 on invalid arguments.
+ */
+int oracle_bwd(const uint16_t *q, const int64_t *q_strides, const uint16_t *k,
+               const int64_t *k_strides, const uint16_t *v,
+               const int64_t *v_strides, const uint16_t *dout, int B, int Hq,
+               int Hkv, int N, int d, int flags, int64_t window_left,
+               int64_t window_right, double softcap,
+               const int32_t *doc_offsets, int doc_stride, double scale,
+               double *out_dq, double *out_dk, double *out_dv)
+{
+    fwd_problem p;
+    int64_t unit;
+    if (B < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv || N < 0 || d <= 0)
+        return -1;
+    if ((flags & ORACLE_DOCS) && (!doc_offsets || doc_stride < 2))
+        return -1;
+    if ((flags & ORACLE_SOFTCAP) && !(softcap > 0.0))
+        return -1;
+    p.q = q; p.k = k; p.v = v;
+    p.qs = q_strides; p.ks = k_strides; p.vs = v_strides;
+    p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.N = N; p.d = d;
+    p.flags = flags; p.wl = window_left; p.wr = window_right;
+    p.softcap = softcap; p.doc_offsets = doc_offsets; p.doc_stride = doc_stride;
+    p.scale = scale;
+    memset(out_dq, 0, sizeof(double) * (size_t)B * Hq * N * d);
+    memset(out_dk, 0, sizeof(double) * (size_t)B * Hkv * N * d);
+    memset(out_dv, 0, sizeof(double) * (size_t)B * Hkv * N * d);
+
+    /* One work unit per (b, KV head): it owns that head's dk and dv. */
+#pragma omp parallel
+    {
+        size_t nn = (size_t)(N > 0 ? N : 1);
+        double *srow = (double *)malloc(sizeof(double) * nn);
+        double *prow = (double *)malloc(sizeof(double) * nn);
+        double *o = (double *)malloc(sizeof(double) * (size_t)d);
+#pragma omp for schedule(dynamic, 1)
+        for (unit = 0; unit < (int64_t)B * Hkv; ++unit) {
+            int b = (int)(unit / Hkv), hk = (int)(unit % Hkv);
+            int group = Hq / Hkv, h, i, j, t;
+            const uint16_t *kb = k + b * k_strides[0] + hk * k_strides[1];
+            const uint16_t *vb = v + b * v_strides[0] + hk * v_strides[1];
+            double *dkb = out_dk + ((int64_t)b * Hkv + hk) * N * d;
+            double *dvb = out_dv + ((int64_t)b * Hkv + hk) * N * d;
+            for (h = hk * group; h < (hk + 1) * group; ++h) {
+                for (i = 0; i < N; ++i) {
+                    double lse, dsum = 0.0;
+                    const uint16_t *qi = q + b * q_strides[0] + h * q_strides[1] + (int64_t)i * q_strides[2];
+                    const uint16_t *doi = dout + (((int64_t)b * Hq + h) * N + i) * d;
+                    double *dqi = out_dq + (((int64_t)b * Hq + h) * N + i) * d;
+                    fwd_row(&p, b, h, i, srow, o, &lse, prow);
+                    if (lse == -INFINITY)
+                        continue; /* no visible key: O = 0 does not depend on the inputs */
+                    for (t = 0; t < d; ++t)
+                        dsum += widen_bf16(doi[t]) * o[t];
+                    for (j = 0; j < N; ++j) {
+                        double dp = 0.0, du;
+                        const uint16_t *kj = kb + (int64_t)j * k_strides[2];
+                        const uint16_t *vj = vb + (int64_t)j * v_strides[2];
+                        if (prow[j] == 0.0)
+                            continue;
+                        for (t = 0; t < d; ++t)
+                            dp += widen_bf16(doi[t]) * widen_bf16(vj[t]);
+                        du = prow[j] * (dp - dsum);
+                        if (flags & ORACLE_SOFTCAP) {
+                            double r = srow[j] / softcap;
+                            du *= 1.0 - r * r;
+                        }
+                        for (t = 0; t < d; ++t) {
+                            dqi[t] += scale * du * widen_bf16(kj[t]);
+                            dkb[(int64_t)j * d + t] += scale * du * widen_bf16(qi[t]);
+                            dvb[(int64_t)j * d + t] += prow[j] * widen_bf16(doi[t]);
+                        }
+                    }
+                }
+            }
+        }
+        free(srow);
+        free(prow);
+        free(o);
+    }
+    return 0;
+}
