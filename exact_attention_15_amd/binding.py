@@ -72,6 +72,10 @@ def _load():
     lib.attn_decode_workspace_size.argtypes = [i32, i32, i32, i32, i32]
     lib.attn_decode.restype = i32
     lib.attn_decode.argtypes = [T, T, T, P, T, P, i32, i32, i32, i32, i32, i32, f32, P, sz, P]
+    lib.attn_bwd_workspace_size.restype = sz
+    lib.attn_bwd_workspace_size.argtypes = [SP, i32, i32, i32]
+    lib.attn_bwd.restype = i32
+    lib.attn_bwd.argtypes = [T, T, T, T, P, T, T, T, T, i32, i32, i32, i32, i32, SP, f32, P, sz, P]
     lib.attn_status_string.restype = ctypes.c_char_p
     lib.attn_status_string.argtypes = [i32]
     lib.attn_last_error.restype = ctypes.c_char_p
@@ -182,6 +186,51 @@ def fwd(q, k, v, *, causal=False, window=None, doc_offsets=None, softcap=None,
                       None if ws is None else ws.data_ptr(), ws_bytes, _stream(q.device))
     _check(st)
     return out, lse
+
+
+def bwd(q, k, v, o, lse, dout, *, causal=False, window=None, doc_offsets=None,
+        softcap=None, scale=None, no_skip=False, spec=None, dq=None, dk=None, dv=None,
+        workspace=None):
+    """Gradients of exact attention.  q, k, v and the mask arguments as given
+    to ``fwd``; o, lse its outputs; dout [B,Hq,N,d] bf16 the gradient of the
+    loss with respect to o.  Returns (dQ [B,Hq,N,d], dK, dV [B,Hkv,N,d]) bf16."""
+    lib = _load()
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout)):
+        _check_bf16(name, t)
+    B, Hq, N, d = q.shape
+    Hkv = k.shape[1]
+    if k.shape != (B, Hkv, N, d) or v.shape != (B, Hkv, N, d):
+        raise ValueError(f"k/v must be [B, Hkv, N, d]; got {tuple(k.shape)} and {tuple(v.shape)}")
+    if o.shape != q.shape or dout.shape != q.shape:
+        raise ValueError("o and dout must have the shape of q")
+    if lse.dtype != torch.float32 or not lse.is_contiguous() or lse.shape != (B, Hq, N):
+        raise TypeError("lse: expected a contiguous fp32 [B, Hq, N] tensor")
+    if spec is None:
+        spec = MaskSpec(causal=causal, window=window, doc_offsets=doc_offsets,
+                        softcap=softcap, no_skip=no_skip)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if dq is None:
+        dq = torch.empty((B, Hq, N, d), dtype=torch.bfloat16, device=q.device)
+    if dk is None:
+        dk = torch.empty((B, Hkv, N, d), dtype=torch.bfloat16, device=q.device)
+    if dv is None:
+        dv = torch.empty((B, Hkv, N, d), dtype=torch.bfloat16, device=q.device)
+    for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+        _check_bf16(name, t)
+    ws_bytes = lib.attn_bwd_workspace_size(spec.ref(), B, Hq, N)
+    if workspace is None or workspace.numel() < ws_bytes:
+        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=q.device)
+    st = lib.attn_bwd(_tensor4(q), _tensor4(k), _tensor4(v), _tensor4(o), lse.data_ptr(),
+                      _tensor4(dout), _tensor4(dq), _tensor4(dk), _tensor4(dv),
+                      B, Hq, Hkv, N, d, spec.ref(), float(scale), workspace.data_ptr(),
+                      ws_bytes, _stream(q.device))
+    _check(st)
+    return dq, dk, dv
+
+
+def bwd_workspace_bytes(B, Hq, N, spec=None) -> int:
+    return _load().attn_bwd_workspace_size(None if spec is None else spec.ref(), B, Hq, N)
 
 
 def decode(q, k_cache, v_cache, lens, *, scale=None, chunk=1024, out=None, lse=None,

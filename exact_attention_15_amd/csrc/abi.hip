@@ -161,6 +161,88 @@ attn_status attn_fwd(attn_tensor q, attn_tensor k, attn_tensor v, attn_tensor o,
     return ATTN_OK;
 }
 
+size_t attn_bwd_workspace_size(const attn_mask_spec *spec, int B, int Hq, int N) {
+    (void)spec;
+    if (B <= 0 || Hq <= 0 || N <= 0) return 0;
+    const size_t rows = size_t(B) * size_t(Hq) * size_t(N);
+    return mask_layout(B, N).bytes + bwd_mask_layout(B, N).bytes + 2 * align256(4 * rows);
+}
+
+attn_status attn_bwd(attn_tensor q, attn_tensor k, attn_tensor v, attn_tensor o, const float *lse,
+                     attn_tensor dout, attn_tensor dq, attn_tensor dk, attn_tensor dv, int B, int Hq, int Hkv,
+                     int N, int d, const attn_mask_spec *spec, float scale, void *workspace, size_t ws_bytes,
+                     void *stream) {
+    if (B < 0 || N < 0) return fail(ATTN_ERR_INVALID, "attn_bwd: B=%d N=%d", B, N);
+    if (Hq <= 0 || Hkv <= 0) return fail(ATTN_ERR_INVALID, "attn_bwd: Hq=%d Hkv=%d", Hq, Hkv);
+    if (Hq % Hkv) return fail(ATTN_ERR_INVALID, "attn_bwd: Hq=%d is not a multiple of Hkv=%d", Hq, Hkv);
+    if (d != 64 && d != 128) return fail(ATTN_ERR_UNSUPPORTED, "attn_bwd: head dim %d (supported: 64, 128)", d);
+    if (!std::isfinite(scale) || !(scale > 0.f)) return fail(ATTN_ERR_INVALID, "attn_bwd: scale must be finite and > 0");
+    attn_status st = check_spec(spec);
+    if (st != ATTN_OK) return st;
+    if (int64_t(B) * N == 0) return ATTN_OK;
+    const attn_tensor *ts[] = {&q, &k, &v, &o, &dout, &dq, &dk, &dv};
+    const char *names[] = {"q", "k", "v", "o", "dout", "dq", "dk", "dv"};
+    for (int i = 0; i < 8; ++i)
+        if ((st = check_tensor(*ts[i], names[i], true)) != ATTN_OK) return st;
+    if (!lse) return fail(ATTN_ERR_INVALID, "attn_bwd: null lse");
+    for (int i = 0; i < 5; ++i)
+        if (ts[i]->stride_n >= (int64_t(1) << 24))
+            return fail(ATTN_ERR_UNSUPPORTED, "attn_bwd: %s token stride must be below 2^24 elements", names[i]);
+    const MaskLayout L = mask_layout(B, N);
+    const BwdMaskLayout BL = bwd_mask_layout(B, N);
+    if (int64_t(B) * L.nqt * Hq > 0x7FFFFFFFLL || int64_t(B) * BL.nkb * Hkv > 0x7FFFFFFFLL)
+        return fail(ATTN_ERR_UNSUPPORTED, "attn_bwd: grid too large");
+    const size_t rows = size_t(B) * size_t(Hq) * size_t(N);
+    const size_t need = attn_bwd_workspace_size(spec, B, Hq, N);
+    if (!workspace || ws_bytes < need)
+        return fail(ATTN_ERR_WORKSPACE, "attn_bwd: workspace needs %zu bytes, got %zu", need,
+                    workspace ? ws_bytes : size_t(0));
+    if (!aligned16(workspace)) return fail(ATTN_ERR_INVALID, "attn_bwd: workspace not 16-byte aligned");
+    const attn_mask_spec sp = spec_or_default(spec);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    char *ws = static_cast<char *>(workspace);
+    char *kv_mask = ws + L.bytes;
+    float *lse2 = reinterpret_cast<float *>(kv_mask + BL.bytes);
+    float *dvec = reinterpret_cast<float *>(kv_mask + BL.bytes + align256(4 * rows));
+    hipError_t e = launch_mask_build(sp, L, ws, s);
+    if (e != hipSuccess) return hip_fail(e, "attn_bwd (mask build)");
+    BwdParams p;
+    p.q = static_cast<const uint16_t *>(q.ptr);
+    p.k = static_cast<const uint16_t *>(k.ptr);
+    p.v = static_cast<const uint16_t *>(v.ptr);
+    p.o = static_cast<const uint16_t *>(o.ptr);
+    p.dout = static_cast<const uint16_t *>(dout.ptr);
+    p.lse = lse;
+    p.lse2 = lse2;
+    p.dvec = dvec;
+    p.dq = static_cast<uint16_t *>(dq.ptr);
+    p.dk = static_cast<uint16_t *>(dk.ptr);
+    p.dv = static_cast<uint16_t *>(dv.ptr);
+    p.q_sb = q.stride_b; p.q_sh = q.stride_h; p.q_sn = q.stride_n;
+    p.k_sb = k.stride_b; p.k_sh = k.stride_h; p.k_sn = k.stride_n;
+    p.v_sb = v.stride_b; p.v_sh = v.stride_h; p.v_sn = v.stride_n;
+    p.o_sb = o.stride_b; p.o_sh = o.stride_h; p.o_sn = o.stride_n;
+    p.do_sb = dout.stride_b; p.do_sh = dout.stride_h; p.do_sn = dout.stride_n;
+    p.dq_sb = dq.stride_b; p.dq_sh = dq.stride_h; p.dq_sn = dq.stride_n;
+    p.dk_sb = dk.stride_b; p.dk_sh = dk.stride_h; p.dk_sn = dk.stride_n;
+    p.dv_sb = dv.stride_b; p.dv_sh = dv.stride_h; p.dv_sn = dv.stride_n;
+    p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.N = N; p.nqt = L.nqt; p.nkt = L.nkt; p.nkb = BL.nkb; p.nqt64 = BL.nqt64;
+    const float log2e = 1.4426950408889634f;
+    p.scale = scale;
+    p.scale_log2 = scale * log2e;
+    const bool softcap = sp.flags & ATTN_MOD_SOFTCAP;
+    p.cap_inv_scale_2log2e = softcap ? 2.f * log2e * (scale / sp.softcap) : 0.f;
+    p.cap_log2 = softcap ? sp.softcap * log2e : 0.f;
+    p.cap_log2_2 = 2.f * p.cap_log2;
+    p.inv_cap_log2 = softcap ? 1.f / p.cap_log2 : 0.f;
+    p.mask = mask_view(ws, L);
+    p.kv_count = reinterpret_cast<const int32_t *>(kv_mask + BL.off_count);
+    p.kv_list = reinterpret_cast<const int32_t *>(kv_mask + BL.off_list);
+    e = launch_bwd(p, d, softcap, sp.flags, L, BL, kv_mask, s);
+    if (e != hipSuccess) return hip_fail(e, "attn_bwd");
+    return ATTN_OK;
+}
+
 size_t attn_decode_workspace_size(int B, int Hq, int T, int d, int chunk) {
     if (B <= 0 || Hq <= 0 || T < 0 || d <= 0 || chunk <= 0) return 0;
     const int nchunk = T > 0 ? (T + chunk - 1) / chunk : 1;

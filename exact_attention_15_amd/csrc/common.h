@@ -79,6 +79,46 @@ struct FwdParams {
 
 hipError_t launch_fwd(const FwdParams &p, int d, bool softcap, hipStream_t stream);
 
+// Backward tiling.  The dQ kernel uses the forward decomposition and block
+// mask.  The dK/dV kernel gives a workgroup BWD_KB keys (4 waves x 32) and
+// streams 64-row query tiles; its per-(b, key block) list of query tiles is
+// the block mask transposed at that granularity: count [B][nkb], list
+// [B][nkb][nqt64] of (query tile << 1) | partial-bit.
+constexpr int BWD_KB = 128;
+struct BwdMaskLayout {
+    int nkb, nqt64;
+    size_t off_count, off_list, bytes;
+};
+inline BwdMaskLayout bwd_mask_layout(int B, int N) {
+    BwdMaskLayout L;
+    L.nkb = (N + BWD_KB - 1) / BWD_KB;
+    L.nqt64 = (N + BLOCK_N - 1) / BLOCK_N;
+    size_t items = size_t(B) * size_t(L.nkb);
+    size_t off = 0;
+    L.off_count = off; off = align256(off + 4 * items);
+    L.off_list = off;  off = align256(off + 4 * items * size_t(L.nqt64));
+    L.bytes = off;
+    return L;
+}
+
+struct BwdParams {
+    const uint16_t *q, *k, *v, *o, *dout;
+    const float *lse;                  // [B][Hq][N] natural log, from the forward
+    float *lse2, *dvec;                // workspace [B][Hq][N]: base-2 LSE (+inf: no key), rowsum(dO * O)
+    uint16_t *dq, *dk, *dv;
+    int64_t q_sb, q_sh, q_sn, k_sb, k_sh, k_sn, v_sb, v_sh, v_sn;
+    int64_t o_sb, o_sh, o_sn, do_sb, do_sh, do_sn;
+    int64_t dq_sb, dq_sh, dq_sn, dk_sb, dk_sh, dk_sn, dv_sb, dv_sh, dv_sn;
+    int B, Hq, Hkv, N, nqt, nkt, nkb, nqt64;
+    float scale, scale_log2;
+    float cap_inv_scale_2log2e, cap_log2, cap_log2_2, inv_cap_log2; // softcap mode only
+    MaskView mask;                     // forward block mask (row intervals, dQ tile lists)
+    const int32_t *kv_count, *kv_list; // transposed lists (dK/dV)
+};
+
+hipError_t launch_bwd(const BwdParams &p, int d, bool softcap, uint32_t flags, const MaskLayout &L,
+                      const BwdMaskLayout &BL, void *kv_mask, hipStream_t stream);
+
 struct DecodeParams {
     const uint16_t *q, *k, *v;
     uint16_t *o;

@@ -156,6 +156,35 @@ attn_status attn_decode(attn_tensor q, attn_tensor k_cache, attn_tensor v_cache,
                         int Hq, int Hkv, int T, int d, int chunk, float scale,
                         void *workspace, size_t ws_bytes, void *stream);
 
+/*
+ * Backward of attn_fwd: the gradients dQ, dK, dV of a loss given its
+ * gradient dO with respect to O.  The probabilities are recomputed tile by
+ * tile from lse instead of being stored (youngju.dev "FlashAttention 논문
+ * 분석", section "Recomputation 전략"); with dP = dO V^T and
+ * D_i = sum_t dO_it O_it, dS = P * (dP - D) (times 1 - tanh^2 of the capped
+ * score under ATTN_MOD_SOFTCAP), dQ = scale dS K, dK = scale dS^T Q,
+ * dV = P^T dO.
+ *   q, k, v, spec, scale, B, Hq, Hkv, N, d: exactly as given to attn_fwd.
+ *   o [B,Hq,N,d] and lse fp32 [B][Hq][N] contiguous: attn_fwd's outputs.
+ *   dout [B,Hq,N,d]: gradient of the loss with respect to o.
+ *   dq [B,Hq,N,d], dk and dv [B,Hkv,N,d]: bf16 outputs, fully overwritten
+ *     (no accumulation into existing values); dk and dv of a KV head sum
+ *     over the Hq/Hkv query heads that share it.  They must not overlap any
+ *     input.  Keys that no query sees get zero gradient, as do rows with no
+ *     visible key.
+ *   workspace: >= attn_bwd_workspace_size(spec, B, Hq, N) bytes, 16-byte
+ *     aligned (the call builds its block masks and per-row data there).
+ *   q, k, v, o and dout token strides must be below 2^24 elements.
+ * Supported: d in {64, 128}; Hq % Hkv == 0.  Errors: ATTN_ERR_INVALID,
+ * ATTN_ERR_UNSUPPORTED, ATTN_ERR_WORKSPACE, ATTN_ERR_HIP.
+ */
+size_t attn_bwd_workspace_size(const attn_mask_spec *spec, int B, int Hq, int N);
+attn_status attn_bwd(attn_tensor q, attn_tensor k, attn_tensor v, attn_tensor o,
+                     const float *lse, attn_tensor dout, attn_tensor dq, attn_tensor dk,
+                     attn_tensor dv, int B, int Hq, int Hkv, int N, int d,
+                     const attn_mask_spec *spec, float scale, void *workspace,
+                     size_t ws_bytes, void *stream);
+
 /* Static description of a status code. */
 const char *attn_status_string(attn_status status);
 /* Detail for the calling thread's most recent non-OK status ("" if none). */

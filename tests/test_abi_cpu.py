@@ -31,6 +31,7 @@ def test_header_declares_the_boundary():
     names = _declared_functions()
     for n in ("attn_fwd", "attn_decode", "attn_mask_build", "attn_mask_bytes",
               "attn_fwd_workspace_size", "attn_decode_workspace_size",
+              "attn_bwd", "attn_bwd_workspace_size",
               "attn_status_string", "attn_last_error"):
         assert n in names
 
@@ -117,3 +118,39 @@ def test_decode_validation_before_launch(lib):
     wide = _t(16, 0, 0, 1 << 20)
     assert lib.attn_decode(t, wide, t, 16, t, ctypes.c_void_p(16), 2, 8, 2, 4096, 128, 1024,
                            ctypes.c_float(0.1), None, 0, None) == b.ATTN_ERR_UNSUPPORTED
+
+
+def test_bwd_workspace_size(lib):
+    # forward block mask + transposed (key-block) mask + two fp32 [B][Hq][N] row arrays
+    from exact_attention_15_amd import binding as b
+
+    def a256(x):
+        return (x + 255) & ~255
+    for B, Hq, N in [(1, 1, 1), (2, 3, 1000), (8, 32, 4096)]:
+        nkb, nqt64 = (N + 127) // 128, (N + 63) // 64
+        kvmask = a256(4 * B * nkb) + a256(4 * B * nkb * nqt64)
+        want = b.mask_layout(B, N)["bytes"] + kvmask + 2 * a256(4 * B * Hq * N)
+        assert lib.attn_bwd_workspace_size(None, B, Hq, N) == want
+    assert lib.attn_bwd_workspace_size(None, 0, 4, 10) == 0
+
+
+def test_bwd_validation_before_launch(lib):
+    from exact_attention_15_amd import binding as b
+    t = _t(16, 0, 0, 128)
+    lse = ctypes.c_void_p(16)
+
+    def call(d=128, Hq=4, Hkv=2, B=1, N=8, scale=0.1, ws=None, ws_bytes=0, dq=t, lse=lse, wide=None):
+        q = wide or t
+        return lib.attn_bwd(q, t, t, t, lse, t, dq, t, t, B, Hq, Hkv, N, d, None,
+                            ctypes.c_float(scale), ws, ws_bytes, None)
+    assert call(d=96) == b.ATTN_ERR_UNSUPPORTED
+    assert call(Hq=3, Hkv=2) == b.ATTN_ERR_INVALID
+    assert call(scale=-1.0) == b.ATTN_ERR_INVALID
+    assert call(dq=_t(0, 0, 0, 128)) == b.ATTN_ERR_INVALID           # null output
+    assert call(dq=_t(24, 0, 0, 128)) == b.ATTN_ERR_INVALID          # misaligned output
+    assert call(lse=None) == b.ATTN_ERR_INVALID
+    assert call(wide=_t(16, 0, 0, 1 << 24)) == b.ATTN_ERR_UNSUPPORTED
+    assert call() == b.ATTN_ERR_WORKSPACE
+    assert call(ws=ctypes.c_void_p(16), ws_bytes=64) == b.ATTN_ERR_WORKSPACE
+    assert call(B=0) == b.ATTN_OK
+    assert call(N=0) == b.ATTN_OK
