@@ -20,6 +20,8 @@ Recipe (the same for every caller):
   (the ``cu_seqlens`` walkthrough in the aegloslab textbook chapter
   "3.7 어텐션 II", section 3.7.6: lengths [3, 5, 2] give [0, 3, 8, 10]).
 * Decode lengths are integers uniform on [1024, 32768] (inclusive).
+* The output gradient dO of a backward workload comes from a generator of
+  its own, ``PCG64(seed)``, drawn N(0,1) after the same rounding.
 """
 from __future__ import annotations
 
@@ -35,6 +37,7 @@ __all__ = [
     "draw_decode_lens",
     "fwd_inputs",
     "decode_inputs",
+    "dout_input",
     "CONFIGS",
 ]
 
@@ -117,6 +120,9 @@ CONFIGS = {
     5: dict(name="decode_b16_gqa32x8_t32768_d128_chunk1024", kind="decode",
             B=16, Hq=32, Hkv=8, T=32768, d=128, factor=1.0, seed=1005,
             chunk=1024),
+    # backward of workload 2: its Q, K, V and a seeded output gradient dO
+    6: dict(name="bwd_causal_b8_h32_n4096_d128", kind="causal", B=8, Hq=32, Hkv=32,
+            N=4096, d=128, factor=0.5, seed=1002, dout_seed=1006),
 }
 
 
@@ -144,3 +150,9 @@ def decode_inputs(seed: int, B: int, Hq: int, Hkv: int, T: int, d: int,
     vc = draw_bf16(rng, (B, Hkv, T, d), factor)
     lens = draw_decode_lens(rng, B, lens_lo, lens_hi)
     return q, kc, vc, lens
+
+
+def dout_input(seed: int, B: int, Hq: int, N: int, d: int) -> np.ndarray:
+    """Output gradient dO [B,Hq,N,d] as bf16 bits, N(0,1)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    return draw_bf16(rng, (B, Hq, N, d), 1.0)

@@ -14,12 +14,15 @@ The same JSON line also carries:
   decode        split-KV decode (split + combine kernels) on B=16, 32 query
                 heads over 8 KV heads, T=32768, lens U[1024, 32768], chunk
                 1024: HBM GB/s of the algorithmic K/V bytes, against 8 TB/s;
+  backward      attn_bwd (dQ, dK, dV) on the headline workload with a seeded
+                output gradient: TFLOP/s at 2.5x the forward's FLOPs (five
+                products per visible pair), against the bf16 MFMA peak;
   configs       every workload's time and throughput;
   cpu_baseline  the fp64 oracle timed on the host cores on a bounded sample
                 of the headline workload (rows of a few heads).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-                       [--configs 1,2,3,4,5]
+                       [--configs 1,2,3,4,5,6]
 """
 from __future__ import annotations
 
@@ -41,6 +44,9 @@ import attn_inputs as gen  # noqa: E402
 METRIC = "fwd attention TFLOPS & % bf16 MFMA peak; decode split-KV HBM GB/s"
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
 HBM_PEAK_GBS = 8000.0           # MI355X HBM3E
+# Backward FLOPs: five products per visible pair (S recomputed, dP, dV, dK,
+# dQ), 2*d each, against the forward's two.
+BWD_FLOP_FACTOR = 2.5
 CSRC = os.path.join(ROOT, "exact_attention_15_amd", "csrc")
 
 # HBM bytes per launch of the dominant kernels, from two rocprofv3 --pmc runs
@@ -53,15 +59,21 @@ CSRC = os.path.join(ROOT, "exact_attention_15_amd", "csrc")
 MEASURED_TRAFFIC = {
     # kernel: (sources, sha256 of their concatenation, bytes per launch, summary)
     "k_attn_fwd_d128": (
-        ["fwd.hip", "common.h"],
-        "a2b0ae6bc9315fe035742fa57d1fc3e66b0a311763af3fd10944499a478173f0",
-        836157840 + 272819200,
+        ["fwd.hip", "tile.h", "common.h"],
+        "47ef7a8c3faa853c52a397c665b9adffad0d42660ca439a3cbed8e98544f6b49",
+        839747644 + 272810736,
         "profiles/k_attn_fwd_d128_causal_b8_h32_n4096_d128.md"),
     "k_decode_split": (
         ["decode.hip", "common.h"],
-        "aea9d6379426116ad0c4ff8a45f27d2f51e177290ddad1fd7cbd96a9c80dd0b0",
-        953145052 + 4415456,
+        "21063eeaf85f9962e5a5ecb13475022807e8e12c3f10b69c7ecc1fbb1713d46b",
+        953909959 + 4412918,
         "profiles/k_decode_split_decode_b16_gqa32x8_t32768_d128.md"),
+    # all kernels of one attn_bwd call (mask_kv, prep, dQ, dK/dV)
+    "attn_bwd_d128": (
+        ["bwd.hip", "tile.h", "common.h"],
+        "d7589acab23067813b00aee1843232f780ab775a27941381870d1a7fc2b19880",
+        11666382900,
+        "profiles/k_bwd_d128_causal_b8_h32_n4096_d128.md"),
 }
 
 
@@ -287,6 +299,31 @@ def bench_decode(ea, w, steps, warmup):
     return dict(ms=ms, dist=dist, gbs=w["bytes"] / (ms * 1e-3) / 1e9)
 
 
+def bench_bwd(ea, w, steps, warmup):
+    """attn_bwd (block masks, row prep, dQ kernel, dK/dV kernel) on the
+    forward workload ``w`` with its own forward outputs and a seeded dO."""
+    import torch
+    c = w["cfg"]
+    B, Hq, Hkv, N, d = c["B"], c["Hq"], c["Hkv"], c["N"], c["d"]
+    dev = w["q"].device
+    spec = ea.MaskSpec(**w["kw_dev"])
+    g = to_dev(gen.dout_input(c["dout_seed"], B, Hq, N, d), dev)
+    o, lse = ea.fwd(w["q"], w["k"], w["v"], spec=spec, scale=w["scale"])
+    dq = torch.empty_like(w["q"])
+    dk = torch.empty_like(w["k"])
+    dv = torch.empty_like(w["v"])
+    ws = torch.empty(ea.bwd_workspace_bytes(B, Hq, N, spec), dtype=torch.uint8, device=dev)
+
+    def step():
+        ea.bwd(w["q"], w["k"], w["v"], o, lse, g, spec=spec, scale=w["scale"], dq=dq, dk=dk, dv=dv,
+               workspace=ws)
+
+    warm_gpu(step)
+    ms = time_launches(step, steps, warmup)
+    dist = time_each(step, max(steps, 10))
+    return dict(ms=ms, dist=dist)
+
+
 def cpu_baseline(w, target_s=15.0):
     """The fp64 oracle on whole (batch row, head) slices of the workload, timed
     on the host cores; throughput in the metric's unit (TFLOP/s).  One slice
@@ -324,7 +361,7 @@ def main(argv=None):
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--configs", default="1,2,3,4,5")
+    ap.add_argument("--configs", default="1,2,3,4,5,6")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run one device-to-device copy of MIB MiB (a known-size "
@@ -356,7 +393,7 @@ def main(argv=None):
     results = {}
     headline = None
     for cid in cfg_ids:
-        if cid == 5:
+        if cid in (5, 6):
             continue
         print(f"[bench] config {cid}: generating inputs", file=sys.stderr, flush=True)
         w = fwd_workload(cid, dev)
@@ -403,6 +440,31 @@ def main(argv=None):
         del wd
         torch.cuda.empty_cache()
 
+    bwd_res = None
+    if 6 in cfg_ids:
+        print("[bench] config 6 (backward of config 2): generating inputs", file=sys.stderr, flush=True)
+        wb = fwd_workload(6, dev)
+        r = bench_bwd(ea, wb, args.steps, args.warmup)
+        c = wb["cfg"]
+        flops = BWD_FLOP_FACTOR * wb["flops"]
+        tf = flops / (r["ms"] * 1e-3) / 1e12
+        bwd_res = {
+            "workload": c["name"], "ms": round(r["ms"], 4),
+            "median_ms": round(r["dist"]["median_ms"], 4), "min_ms": round(r["dist"]["min_ms"], 4),
+            "p90_ms": round(r["dist"]["p90_ms"], 4),
+            "flops": flops, "tflops": round(tf, 2),
+            "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
+                         "traffic": measured_traffic("attn_bwd_d128"),
+                         "kernels": "k_bwd_mask_kv + k_bwd_prep + k_bwd_dq + k_bwd_dkdv and the "
+                                    "forward block mask (one attn_bwd call, timed together)"},
+        }
+        results[c["name"]] = {"ms": bwd_res["ms"], "tflops": bwd_res["tflops"],
+                              "frac_mfma_peak": bwd_res["roofline"]["frac"]}
+        print(f"[bench] config 6: {r['ms']:.3f} ms, {tf:.1f} TFLOP/s", file=sys.stderr, flush=True)
+        del wb
+        torch.cuda.empty_cache()
+
     out = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
            "data": "synthetic: seeded N(0,1) bf16 inputs (x0.5 for the headline workload)"}
@@ -428,6 +490,8 @@ def main(argv=None):
             out["cpu_baseline"] = cpu_baseline(w)
     if decode_res is not None:
         out["decode"] = decode_res
+    if bwd_res is not None:
+        out["backward"] = bwd_res
     out["configs"] = results
     print(json.dumps(out), flush=True)
     return 0

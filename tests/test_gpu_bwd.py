@@ -47,9 +47,7 @@ def ea():
 
 def _grad_inputs(seed, B, Hq, Hkv, N, d, factor):
     q, k, v, _ = gen.fwd_inputs(seed, B, Hq, Hkv, N, d, factor)
-    rng = np.random.Generator(np.random.PCG64(seed + 7919))
-    dout = gen.draw_bf16(rng, (B, Hq, N, d), 1.0)
-    return q, k, v, dout
+    return q, k, v, gen.dout_input(seed + 7919, B, Hq, N, d)
 
 
 def compare_grads(got, ref, lse, what):
