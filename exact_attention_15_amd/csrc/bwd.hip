@@ -408,9 +408,21 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdParams &p) {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int col = lane & 31, half = lane >> 5;
 
-    const int kb = bid % p.nkb;
-    const int hk = (bid / p.nkb) % p.Hkv;
-    const int b = bid / (p.nkb * p.Hkv);
+    // Work assignment: the key blocks of one (b, KV head) share every Q and
+    // dO tile, so they run on one XCD (workgroups are dispatched round-robin
+    // over the 8 XCDs by id % 8, each XCD with its own L2) in ascending
+    // block order, which is heaviest first under a causal mask.
+    const int ngroups = p.B * p.Hkv;
+    int group, kb;
+    if ((ngroups & 7) == 0) {
+        const int x = bid & 7, j = bid >> 3;
+        group = x + 8 * (j / p.nkb);
+        kb = j % p.nkb;
+    } else {
+        group = bid / p.nkb;
+        kb = bid % p.nkb;
+    }
+    const int b = group / p.Hkv, hk = group % p.Hkv;
     const int G = p.Hq / p.Hkv;
     const int key = kb * BWD_KB + wave * 32 + col;
     const bool key_ok = key < p.N;
@@ -474,9 +486,12 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdParams &p) {
                 rowd + arr * 256 + 4 * (32 * kbk + 8 * i + 4 * half));
         };
 
-        // S = Q K^T (lane = key, registers = query rows)
+        // S = Q K^T (lane = key, registers = query rows), then dP = dO V^T,
+        // whose MFMAs run while the probabilities are formed
         f32x16_t s0, s1;
         tl.rows_times_frag(qs, kf, s0, s1);
+        f32x16_t g0, g1;
+        tl.rows_times_frag(gs, vf, g0, g1);
         float pr[32], fac[32];
 #pragma unroll
         for (int kbk = 0; kbk < 2; ++kbk)
@@ -518,9 +533,7 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdParams &p) {
         u32x4_t pk[4];
         pack4(pr, pk);
         tl.tile_t_times(gs, pk, adv);
-        // dP = dO V^T, dS = P (dP - D) * cap factor
-        f32x16_t g0, g1;
-        tl.rows_times_frag(gs, vf, g0, g1);
+        // dS = P (dP - D) * cap factor
         float ds[32];
 #pragma unroll
         for (int kbk = 0; kbk < 2; ++kbk)
