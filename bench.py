@@ -61,18 +61,18 @@ MEASURED_TRAFFIC = {
     "k_attn_fwd_d128": (
         ["fwd.hip", "tile.h", "common.h"],
         "47ef7a8c3faa853c52a397c665b9adffad0d42660ca439a3cbed8e98544f6b49",
-        839747644 + 272810736,
+        1111661296,
         "profiles/k_attn_fwd_d128_causal_b8_h32_n4096_d128.md"),
     "k_decode_split": (
         ["decode.hip", "common.h"],
         "21063eeaf85f9962e5a5ecb13475022807e8e12c3f10b69c7ecc1fbb1713d46b",
-        953909959 + 4412918,
+        958322629,
         "profiles/k_decode_split_decode_b16_gqa32x8_t32768_d128.md"),
     # all kernels of one attn_bwd call (mask_kv, prep, dQ, dK/dV)
     "attn_bwd_d128": (
         ["bwd.hip", "tile.h", "common.h"],
-        "d7589acab23067813b00aee1843232f780ab775a27941381870d1a7fc2b19880",
-        11666382900,
+        "5619618c6226af9b37d30f53dea4469492ea8e11610d50f81072cdc24275f232",
+        3564192937,
         "profiles/k_bwd_d128_causal_b8_h32_n4096_d128.md"),
 }
 

@@ -569,13 +569,14 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdParams &p) {
 }
 
 // Register budgets: the dQ kernel keeps Q and dO fragments and a d x 32
-// accumulator per wave (two waves per SIMD at d = 64, one at d = 128); the dK/dV
-// kernel keeps K and V fragments and two accumulators (one wave per SIMD,
-// accumulators in AGPRs).
+// accumulator per wave; two waves per SIMD fit except with the soft cap at
+// d = 128 (at d = 128 without the cap a few registers spill, which costs
+// less than losing the second wave).  The dK/dV kernel keeps K and V
+// fragments and two accumulators: one wave per SIMD, accumulators in AGPRs.
 #define EXATTN_BWD_KERNELS(SUFFIX, D, SOFTCAP, DQ_WAVES)                                                     \
     __global__ __launch_bounds__(256, DQ_WAVES) void k_bwd_dq_##SUFFIX(BwdParams p) { bwd_dq_body<D, SOFTCAP>(p); } \
     __global__ __launch_bounds__(256, 1) void k_bwd_dkdv_##SUFFIX(BwdParams p) { bwd_dkdv_body<D, SOFTCAP>(p); }
-EXATTN_BWD_KERNELS(d128, 128, false, 1)
+EXATTN_BWD_KERNELS(d128, 128, false, 2)
 EXATTN_BWD_KERNELS(d128_softcap, 128, true, 1)
 EXATTN_BWD_KERNELS(d64, 64, false, 2)
 EXATTN_BWD_KERNELS(d64_softcap, 64, true, 2)
