@@ -17,12 +17,15 @@ The same JSON line also carries:
   backward      attn_bwd (dQ, dK, dV) on the headline workload with a seeded
                 output gradient: TFLOP/s at 2.5x the forward's FLOPs (five
                 products per visible pair), against the bf16 MFMA peak;
+  varlen        attn_fwd_varlen on the GQA document workload packed into
+                [B*N, H, d] with its documents as the sequences (config 7,
+                run with config 4);
   configs       every workload's time and throughput;
   cpu_baseline  the fp64 oracle timed on the host cores on a bounded sample
                 of the headline workload (rows of a few heads).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-                       [--configs 1,2,3,4,5,6]
+                       [--configs 1,2,3,4,5,6,7]
 """
 from __future__ import annotations
 
@@ -324,6 +327,29 @@ def bench_bwd(ea, w, steps, warmup):
     return dict(ms=ms, dist=dist)
 
 
+def bench_varlen(ea, w, steps, warmup):
+    """attn_fwd_varlen (block mask for the packed sequences + forward kernel)
+    on the document workload ``w`` packed into [B*N, H, d] with its documents
+    as the sequences."""
+    import torch
+    c = w["cfg"]
+    B, N = c["B"], c["N"]
+    pk = lambda t: t.transpose(1, 2).reshape(B * N, t.shape[1], t.shape[3]).contiguous()
+    q, k, v = pk(w["q"]), pk(w["k"]), pk(w["v"])
+    cu = np.concatenate([w["doc_rows"][b][:-1] + b * N for b in range(B)] + [[B * N]]).astype(np.int32)
+    cud = torch.from_numpy(cu).to(q.device)
+    o = torch.empty_like(q)
+    lse = torch.empty((c["Hq"], B * N), dtype=torch.float32, device=q.device)
+    ws = torch.empty(ea.fwd_varlen_workspace_bytes(B * N, B * N), dtype=torch.uint8, device=q.device)
+
+    def step():
+        ea.fwd_varlen(q, k, v, cud, cud, causal=True, scale=w["scale"], out=o, lse=lse, workspace=ws)
+
+    warm_gpu(step)
+    ms = time_launches(step, steps, warmup)
+    return dict(ms=ms, nseq=len(cu) - 1, tflops=w["flops"] / (ms * 1e-3) / 1e12)
+
+
 def cpu_baseline(w, target_s=15.0):
     """The fp64 oracle on whole (batch row, head) slices of the workload, timed
     on the host cores; throughput in the metric's unit (TFLOP/s).  One slice
@@ -361,7 +387,7 @@ def main(argv=None):
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--configs", default="1,2,3,4,5,6")
+    ap.add_argument("--configs", default="1,2,3,4,5,6,7")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run one device-to-device copy of MIB MiB (a known-size "
@@ -392,8 +418,9 @@ def main(argv=None):
 
     results = {}
     headline = None
+    varlen_res = None
     for cid in cfg_ids:
-        if cid in (5, 6):
+        if cid in (5, 6, 7):
             continue
         print(f"[bench] config {cid}: generating inputs", file=sys.stderr, flush=True)
         w = fwd_workload(cid, dev)
@@ -412,6 +439,20 @@ def main(argv=None):
         }
         print(f"[bench] config {cid} {c['name']}: {r['ms_kernel']:.3f} ms kernel, "
               f"{r['tflops_kernel']:.1f} TFLOP/s", file=sys.stderr, flush=True)
+        if cid == 4 and 7 in cfg_ids:
+            rv = bench_varlen(ea, w, args.steps, args.warmup)
+            varlen_res = {
+                "workload": "varlen_" + c["name"], "sequences": rv["nseq"],
+                "ms": round(rv["ms"], 4), "tflops": round(rv["tflops"], 2),
+                "roofline": {"bound": "mfma", "achieved": round(rv["tflops"], 2),
+                             "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                             "frac": round(rv["tflops"] / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                             "kernels": "k_mask_tiles + k_mask_order + k_attn_fwd_d128 (one "
+                                        "attn_fwd_varlen call, timed together)"},
+            }
+            results[varlen_res["workload"]] = {"ms": varlen_res["ms"], "tflops": varlen_res["tflops"]}
+            print(f"[bench] config 7 (config 4 packed, varlen): {rv['ms']:.3f} ms, "
+                  f"{rv['tflops']:.1f} TFLOP/s", file=sys.stderr, flush=True)
         if cid == 2:
             headline = (w, r)
         else:
@@ -492,6 +533,8 @@ def main(argv=None):
         out["decode"] = decode_res
     if bwd_res is not None:
         out["backward"] = bwd_res
+    if varlen_res is not None:
+        out["varlen"] = varlen_res
     out["configs"] = results
     print(json.dumps(out), flush=True)
     return 0

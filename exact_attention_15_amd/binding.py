@@ -68,6 +68,10 @@ def _load():
     lib.attn_fwd_workspace_size.argtypes = [SP, i32, i32]
     lib.attn_fwd.restype = i32
     lib.attn_fwd.argtypes = [T, T, T, T, P, i32, i32, i32, i32, i32, SP, f32, P, P, sz, P]
+    lib.attn_fwd_varlen_workspace_size.restype = sz
+    lib.attn_fwd_varlen_workspace_size.argtypes = [i32, i32]
+    lib.attn_fwd_varlen.restype = i32
+    lib.attn_fwd_varlen.argtypes = [T, T, T, T, P, P, P, i32, i32, i32, i32, i32, i32, SP, f32, P, sz, P]
     lib.attn_decode_workspace_size.restype = sz
     lib.attn_decode_workspace_size.argtypes = [i32, i32, i32, i32, i32]
     lib.attn_decode.restype = i32
@@ -105,7 +109,7 @@ def _tensor4(t: torch.Tensor) -> AttnTensor:
 def _check_bf16(name, t):
     if not t.is_cuda or t.dtype != torch.bfloat16:
         raise TypeError(f"{name}: expected a bf16 tensor on a GPU")
-    if t.stride(-1) != 1:
+    if t.numel() and t.stride(-1) != 1:
         raise ValueError(f"{name}: the head dimension must be contiguous")
 
 
@@ -186,6 +190,52 @@ def fwd(q, k, v, *, causal=False, window=None, doc_offsets=None, softcap=None,
                       None if ws is None else ws.data_ptr(), ws_bytes, _stream(q.device))
     _check(st)
     return out, lse
+
+
+def _tensor3(t: torch.Tensor) -> AttnTensor:
+    if t.dim() != 3:
+        raise ValueError("expected a 3-D tensor [total, H, d]")
+    return AttnTensor(t.data_ptr(), 0, t.stride(1), t.stride(0))
+
+
+def fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, *, causal=False, window=None,
+               softcap=None, scale=None, no_skip=False, out=None, lse=None, workspace=None):
+    """Exact attention over packed variable-length sequences.  q [total_q, Hq, d],
+    k/v [total_k, Hkv, d] bf16; cu_seqlens_q/k int32 [nseq + 1] on the GPU
+    (cumulative lengths).  Returns (O [total_q, Hq, d] bf16, LSE [Hq, total_q] fp32)."""
+    lib = _load()
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check_bf16(name, t)
+    tq, Hq, d = q.shape
+    tk, Hkv = k.shape[0], k.shape[1]
+    if k.shape != (tk, Hkv, d) or v.shape != (tk, Hkv, d):
+        raise ValueError(f"k/v must be [total_k, Hkv, d]; got {tuple(k.shape)} and {tuple(v.shape)}")
+    for name, c in (("cu_seqlens_q", cu_seqlens_q), ("cu_seqlens_k", cu_seqlens_k)):
+        if c.dtype != torch.int32 or not c.is_cuda or c.dim() != 1 or not c.is_contiguous():
+            raise TypeError(f"{name}: expected a contiguous int32 [nseq + 1] GPU tensor")
+    if cu_seqlens_q.numel() != cu_seqlens_k.numel() or cu_seqlens_q.numel() < 1:
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must both hold nseq + 1 >= 1 entries")
+    nseq = cu_seqlens_q.numel() - 1
+    spec = MaskSpec(causal=causal, window=window, softcap=softcap, no_skip=no_skip)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty((tq, Hq, d), dtype=torch.bfloat16, device=q.device)
+    if lse is None:
+        lse = torch.empty((Hq, tq), dtype=torch.float32, device=q.device)
+    ws_bytes = lib.attn_fwd_varlen_workspace_size(tq, tk)
+    if workspace is None or workspace.numel() < ws_bytes:
+        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=q.device)
+    st = lib.attn_fwd_varlen(_tensor3(q), _tensor3(k), _tensor3(v), _tensor3(out), lse.data_ptr(),
+                             cu_seqlens_q.data_ptr(), cu_seqlens_k.data_ptr(), nseq, tq, tk, Hq, Hkv,
+                             d, spec.ref(), float(scale), workspace.data_ptr(), ws_bytes,
+                             _stream(q.device))
+    _check(st)
+    return out, lse
+
+
+def fwd_varlen_workspace_bytes(total_q, total_k) -> int:
+    return _load().attn_fwd_varlen_workspace_size(total_q, total_k)
 
 
 def bwd(q, k, v, o, lse, dout, *, causal=False, window=None, doc_offsets=None,

@@ -56,6 +56,16 @@ attn_status check_spec(const attn_mask_spec *spec) {
     return ATTN_OK;
 }
 
+// Scale and soft-cap constants of the score path, in base-2 units.
+void set_score_params(FwdParams &p, const attn_mask_spec &sp, float scale) {
+    const float log2e = 1.4426950408889634f;
+    p.scale_log2 = scale * log2e;
+    const bool softcap = sp.flags & ATTN_MOD_SOFTCAP;
+    p.cap_inv_scale_2log2e = softcap ? 2.f * log2e * (scale / sp.softcap) : 0.f;
+    p.cap_log2 = softcap ? sp.softcap * log2e : 0.f;
+    p.cap_log2_2 = 2.f * p.cap_log2;
+}
+
 attn_mask_spec spec_or_default(const attn_mask_spec *spec) {
     attn_mask_spec s;
     std::memset(&s, 0, sizeof s);
@@ -148,16 +158,74 @@ attn_status attn_fwd(attn_tensor q, attn_tensor k, attn_tensor v, attn_tensor o,
     p.k_sb = k.stride_b; p.k_sh = k.stride_h; p.k_sn = k.stride_n;
     p.v_sb = v.stride_b; p.v_sh = v.stride_h; p.v_sn = v.stride_n;
     p.o_sb = o.stride_b; p.o_sh = o.stride_h; p.o_sn = o.stride_n;
-    p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.N = N; p.nqt = L.nqt; p.nkt = L.nkt;
-    const float log2e = 1.4426950408889634f;
-    p.scale_log2 = scale * log2e;
-    const bool softcap = sp.flags & ATTN_MOD_SOFTCAP;
-    p.cap_inv_scale_2log2e = softcap ? 2.f * log2e * (scale / sp.softcap) : 0.f;
-    p.cap_log2 = softcap ? sp.softcap * log2e : 0.f;
-    p.cap_log2_2 = 2.f * p.cap_log2;
+    p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.N = N; p.Nk = N; p.nqt = L.nqt; p.nkt = L.nkt;
+    set_score_params(p, sp, scale);
     p.mask = mask_view(mask, L);
-    hipError_t e = launch_fwd(p, d, softcap, s);
+    hipError_t e = launch_fwd(p, d, sp.flags & ATTN_MOD_SOFTCAP, s);
     if (e != hipSuccess) return hip_fail(e, "attn_fwd");
+    return ATTN_OK;
+}
+
+size_t attn_fwd_varlen_workspace_size(int total_q, int total_k) {
+    if (total_q <= 0 || total_k < 0) return 0;
+    return mask_layout(1, total_q, total_k).bytes;
+}
+
+attn_status attn_fwd_varlen(attn_tensor q, attn_tensor k, attn_tensor v, attn_tensor o, float *lse,
+                            const int32_t *cu_seqlens_q, const int32_t *cu_seqlens_k, int nseq, int total_q,
+                            int total_k, int Hq, int Hkv, int d, const attn_mask_spec *spec, float scale,
+                            void *workspace, size_t ws_bytes, void *stream) {
+    if (nseq < 0 || total_q < 0 || total_k < 0)
+        return fail(ATTN_ERR_INVALID, "attn_fwd_varlen: nseq=%d total_q=%d total_k=%d", nseq, total_q, total_k);
+    if (Hq <= 0 || Hkv <= 0) return fail(ATTN_ERR_INVALID, "attn_fwd_varlen: Hq=%d Hkv=%d", Hq, Hkv);
+    if (Hq % Hkv) return fail(ATTN_ERR_INVALID, "attn_fwd_varlen: Hq=%d is not a multiple of Hkv=%d", Hq, Hkv);
+    if (d != 64 && d != 128)
+        return fail(ATTN_ERR_UNSUPPORTED, "attn_fwd_varlen: head dim %d (supported: 64, 128)", d);
+    if (!std::isfinite(scale) || !(scale > 0.f))
+        return fail(ATTN_ERR_INVALID, "attn_fwd_varlen: scale must be finite and > 0");
+    attn_status st = check_spec(spec);
+    if (st != ATTN_OK) return st;
+    if (spec && (spec->flags & ATTN_MASK_DOCS))
+        return fail(ATTN_ERR_INVALID, "attn_fwd_varlen: ATTN_MASK_DOCS does not apply (sequences come from cu_seqlens)");
+    if (total_q == 0) return ATTN_OK;
+    if (nseq == 0) return fail(ATTN_ERR_INVALID, "attn_fwd_varlen: total_q=%d rows but no sequence", total_q);
+    if (!cu_seqlens_q || !cu_seqlens_k) return fail(ATTN_ERR_INVALID, "attn_fwd_varlen: null cu_seqlens");
+    if ((st = check_tensor(q, "q", true)) != ATTN_OK) return st;
+    if ((st = check_tensor(o, "o", true)) != ATTN_OK) return st;
+    if (total_k > 0) {
+        if ((st = check_tensor(k, "k", true)) != ATTN_OK) return st;
+        if ((st = check_tensor(v, "v", true)) != ATTN_OK) return st;
+    }
+    if (!lse) return fail(ATTN_ERR_INVALID, "attn_fwd_varlen: null lse");
+    if (k.stride_n >= (int64_t(1) << 24) || v.stride_n >= (int64_t(1) << 24))
+        return fail(ATTN_ERR_UNSUPPORTED, "attn_fwd_varlen: k/v token stride must be below 2^24 elements");
+    const MaskLayout L = mask_layout(1, total_q, total_k);
+    if (int64_t(L.nqt) * Hq > 0x7FFFFFFFLL) return fail(ATTN_ERR_UNSUPPORTED, "attn_fwd_varlen: grid too large");
+    if (!workspace || ws_bytes < L.bytes)
+        return fail(ATTN_ERR_WORKSPACE, "attn_fwd_varlen: workspace needs %zu bytes, got %zu", L.bytes,
+                    workspace ? ws_bytes : size_t(0));
+    if (!aligned16(workspace)) return fail(ATTN_ERR_INVALID, "attn_fwd_varlen: workspace not 16-byte aligned");
+    const attn_mask_spec sp = spec_or_default(spec);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = launch_mask_build(sp, L, workspace, s, VarlenView{cu_seqlens_q, cu_seqlens_k, nseq});
+    if (e != hipSuccess) return hip_fail(e, "attn_fwd_varlen (mask build)");
+    // With no keys at all every row is empty and no key tile is listed; the
+    // kernel then never reads k or v.
+    FwdParams p;
+    p.q = static_cast<const uint16_t *>(q.ptr);
+    p.k = static_cast<const uint16_t *>(total_k > 0 ? k.ptr : q.ptr);
+    p.v = static_cast<const uint16_t *>(total_k > 0 ? v.ptr : q.ptr);
+    p.o = static_cast<uint16_t *>(o.ptr);
+    p.lse = lse;
+    p.q_sb = 0; p.q_sh = q.stride_h; p.q_sn = q.stride_n;
+    p.k_sb = 0; p.k_sh = k.stride_h; p.k_sn = k.stride_n;
+    p.v_sb = 0; p.v_sh = v.stride_h; p.v_sn = v.stride_n;
+    p.o_sb = 0; p.o_sh = o.stride_h; p.o_sn = o.stride_n;
+    p.B = 1; p.Hq = Hq; p.Hkv = Hkv; p.N = total_q; p.Nk = total_k; p.nqt = L.nqt; p.nkt = L.nkt;
+    set_score_params(p, sp, scale);
+    p.mask = mask_view(workspace, L);
+    e = launch_fwd(p, d, sp.flags & ATTN_MOD_SOFTCAP, s);
+    if (e != hipSuccess) return hip_fail(e, "attn_fwd_varlen");
     return ATTN_OK;
 }
 

@@ -16,20 +16,23 @@ constexpr int BLOCK_N = 64;
 // Block-mask entry: (key tile index << 1) | partial-bit.
 constexpr int32_t TILE_PARTIAL = 1;
 
-// Device layout of a block mask (all int32, each section 256-byte aligned).
+// Device layout of a block mask (all int32, each section 256-byte aligned)
+// for B batch rows of N query rows over Nk keys (Nk = N except for packed
+// variable-length input).
 struct MaskLayout {
-    int B, N, nqt, nkt;
+    int B, N, Nk, nqt, nkt;
     size_t off_lo, off_hi, off_count, off_list, off_order, bytes;
 };
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
-inline MaskLayout mask_layout(int B, int N) {
+inline MaskLayout mask_layout(int B, int N, int Nk = -1) {
     MaskLayout L;
     L.B = B;
     L.N = N;
+    L.Nk = Nk < 0 ? N : Nk;
     L.nqt = (N + BLOCK_M - 1) / BLOCK_M;
-    L.nkt = (N + BLOCK_N - 1) / BLOCK_N;
+    L.nkt = (L.Nk + BLOCK_N - 1) / BLOCK_N;
     size_t rows = size_t(B) * size_t(N);
     size_t items = size_t(B) * size_t(L.nqt);
     size_t off = 0;
@@ -57,9 +60,17 @@ inline MaskView mask_view(const void *base, const MaskLayout &L) {
     return v;
 }
 
+// Packed variable-length sequences (one batch row): sequence s holds query
+// rows [cu_q[s], cu_q[s+1]) and keys [cu_k[s], cu_k[s+1]).  Null cu_q means
+// a regular [B, N] layout.
+struct VarlenView {
+    const int32_t *cu_q, *cu_k;
+    int nseq;
+};
+
 // Launchers (each returns hipSuccess or the launch error).
 hipError_t launch_mask_build(const attn_mask_spec &spec, const MaskLayout &L,
-                             void *out, hipStream_t stream);
+                             void *out, hipStream_t stream, VarlenView vl = VarlenView{nullptr, nullptr, 0});
 
 struct FwdParams {
     const uint16_t *q, *k, *v;
@@ -70,6 +81,7 @@ struct FwdParams {
     int64_t v_sb, v_sh, v_sn;
     int64_t o_sb, o_sh, o_sn;
     int B, Hq, Hkv, N, nqt, nkt;
+    int Nk;              // keys per batch row (N except for packed variable-length input)
     float scale_log2;    // scale * log2(e): scores in base-2 units
     float cap_inv_scale_2log2e; // 2 * log2(e) * scale / c (softcap mode only)
     float cap_log2;             // c * log2(e)     (softcap mode only)

@@ -134,14 +134,14 @@ __device__ __forceinline__ void attn_fwd_body(const FwdParams &p) {
         const uint16_t *vt_base = vbase + int64_t(key0) * p.v_sn;
         lds_u8 *kdst = smem + stage * C::STAGE_BYTES + C::LOADS * wave * 1024;
         lds_u8 *vdst = kdst + C::TILE_BYTES;
-        if (key0 + BLOCK_N <= p.N) {
+        if (key0 + BLOCK_N <= p.Nk) {
 #pragma unroll
             for (int u = 0; u < C::LOADS; ++u) {
                 dma16_saddr(kt_base, ld_koff[u], lds_addr(kdst + u * 1024));
                 dma16_saddr(vt_base, ld_voff[u], lds_addr(vdst + u * 1024));
             }
         } else {
-            const int last = p.N - 1 - key0; // rows past N re-read row N-1 (always masked)
+            const int last = p.Nk - 1 - key0; // rows past Nk re-read row Nk-1 (always masked)
 #pragma unroll
             for (int u = 0; u < C::LOADS; ++u) {
                 const int r = min(ld_row(u), last);

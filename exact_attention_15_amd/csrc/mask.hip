@@ -3,7 +3,8 @@
 // tiles of each batch row.
 //
 // Every mask the library supports (causal, sliding window, document
-// boundaries, and their combinations) leaves each query row i one interval
+// boundaries, packed variable-length sequences, and their combinations)
+// leaves each query row i one interval
 // [lo_i, hi_i] of visible keys.  The block mask precomputes, per 128-row
 // query tile, which 64-key tiles hold any visible key, so the forward kernel
 // never visits fully masked tiles (it-trends-board "PyTorch FlexAttention
@@ -14,11 +15,58 @@
 
 namespace exattn {
 
+// Packed variable-length input: query row i belongs to the sequence s with
+// cu_q[s] <= i < cu_q[s+1] and sees that sequence's keys [cu_k[s],
+// cu_k[s+1]).  With Lq queries and Lk keys in the sequence, query iq lines
+// up with key iq + Lk - Lq (the last query with the last key), and the
+// causal limit and the window are taken about that key.  Offsets are
+// clamped into [0, N] and [0, Nk], so malformed ones cannot move an
+// interval outside the keys that exist.
+__device__ __forceinline__ void varlen_interval(const attn_mask_spec &spec, const VarlenView &vl, int N, int Nk,
+                                                int i, int64_t &lo, int64_t &hi) {
+    // last sequence s in [0, nseq) with cu_q[s] <= i
+    int a = 0, z = vl.nseq - 1;
+    if (z < 0 || vl.cu_q[0] > i) {
+        lo = 1;
+        hi = 0;
+        return;
+    }
+    while (a < z) {
+        const int mid = (a + z + 1) >> 1;
+        if (vl.cu_q[mid] <= i) a = mid; else z = mid - 1;
+    }
+    const int64_t q0 = min(max(int64_t(vl.cu_q[a]), int64_t(0)), int64_t(N));
+    const int64_t q1 = min(max(int64_t(vl.cu_q[a + 1]), q0), int64_t(N));
+    const int64_t k0 = min(max(int64_t(vl.cu_k[a]), int64_t(0)), int64_t(Nk));
+    const int64_t k1 = min(max(int64_t(vl.cu_k[a + 1]), k0), int64_t(Nk));
+    if (i >= q1) { // past the last sequence's queries
+        lo = 1;
+        hi = 0;
+        return;
+    }
+    const int64_t diag = (i - q0) + (k1 - k0) - (q1 - q0); // local key on this query's diagonal
+    int64_t l = 0, h = k1 - k0 - 1;
+    if (spec.flags & ATTN_MASK_CAUSAL) h = min(h, diag);
+    if (spec.flags & ATTN_MASK_WINDOW) {
+        l = max(l, diag - spec.window_left);
+        h = min(h, diag + spec.window_right);
+    }
+    lo = k0 + l;
+    hi = k0 + h;
+}
+
 // The visible interval [lo, hi] of query row i of batch row b (lo > hi when
 // no key is visible: then lo = 1, hi = 0).
-__device__ __forceinline__ void row_interval(const attn_mask_spec &spec, int b, int N, int i, int &lo_out,
-                                             int &hi_out) {
+__device__ __forceinline__ void row_interval(const attn_mask_spec &spec, const VarlenView &vl, int b, int N, int Nk,
+                                             int i, int &lo_out, int &hi_out) {
     int64_t lo = 0, hi = int64_t(N) - 1;
+    if (vl.cu_q) {
+        varlen_interval(spec, vl, N, Nk, i, lo, hi);
+        if (lo > hi) { lo = 1; hi = 0; }
+        lo_out = int(lo);
+        hi_out = int(hi);
+        return;
+    }
     if (spec.flags & ATTN_MASK_CAUSAL) hi = min(hi, int64_t(i));
     if (spec.flags & ATTN_MASK_WINDOW) {
         lo = max(lo, int64_t(i) - spec.window_left);
@@ -53,8 +101,8 @@ __device__ __forceinline__ void row_interval(const attn_mask_spec &spec, int b, 
 // lane tests two of the 128 rows and two ballots give "any row sees a key"
 // and "every row sees every key"; lane j keeps tile j's result.  The visited
 // tiles are then written in key order with a ballot/popcount compaction.
-__global__ __launch_bounds__(256) void k_mask_tiles(attn_mask_spec spec, int N, int nqt, int nkt,
-                                                    int32_t *lo_out, int32_t *hi_out, int32_t *count_out,
+__global__ __launch_bounds__(256) void k_mask_tiles(attn_mask_spec spec, VarlenView vl, int N, int Nk, int nqt,
+                                                    int nkt, int32_t *lo_out, int32_t *hi_out, int32_t *count_out,
                                                     int32_t *list_out) {
     __shared__ int32_t s_lo[BLOCK_M], s_hi[BLOCK_M];
     __shared__ int32_t s_wcnt[4];
@@ -65,7 +113,7 @@ __global__ __launch_bounds__(256) void k_mask_tiles(attn_mask_spec spec, int N, 
         int lo = 1, hi = 0;
         const int row = r0 + t;
         if (row < N) {
-            row_interval(spec, b, N, row, lo, hi);
+            row_interval(spec, vl, b, N, Nk, row, lo, hi);
             lo_out[int64_t(b) * N + row] = lo;
             hi_out[int64_t(b) * N + row] = hi;
         }
@@ -136,15 +184,15 @@ __global__ __launch_bounds__(1024) void k_mask_order(int nqt, const int32_t *cou
 }
 
 hipError_t launch_mask_build(const attn_mask_spec &spec, const MaskLayout &L, void *out,
-                             hipStream_t stream) {
+                             hipStream_t stream, VarlenView vl) {
     char *base = static_cast<char *>(out);
     int32_t *lo = reinterpret_cast<int32_t *>(base + L.off_lo);
     int32_t *hi = reinterpret_cast<int32_t *>(base + L.off_hi);
     int32_t *cnt = reinterpret_cast<int32_t *>(base + L.off_count);
     int32_t *list = reinterpret_cast<int32_t *>(base + L.off_list);
     int32_t *order = reinterpret_cast<int32_t *>(base + L.off_order);
-    hipLaunchKernelGGL(k_mask_tiles, dim3(L.nqt, L.B), dim3(256), 0, stream, spec, L.N, L.nqt, L.nkt, lo, hi,
-                       cnt, list);
+    hipLaunchKernelGGL(k_mask_tiles, dim3(L.nqt, L.B), dim3(256), 0, stream, spec, vl, L.N, L.Nk, L.nqt, L.nkt,
+                       lo, hi, cnt, list);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(k_mask_order, dim3(L.B), dim3(1024), 0, stream, L.nqt, cnt, order);

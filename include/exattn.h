@@ -132,6 +132,39 @@ attn_status attn_fwd(attn_tensor q, attn_tensor k, attn_tensor v, attn_tensor o,
                      void *stream);
 
 /*
+ * Forward attention over packed variable-length sequences (no padding):
+ * the flash-attn varlen form of aegloslab "3.7 어텐션 II", section 3.7.6.
+ * Sequence s owns query rows [cu_seqlens_q[s], cu_seqlens_q[s+1]) and keys
+ * [cu_seqlens_k[s], cu_seqlens_k[s+1]); a query sees only its own
+ * sequence's keys.
+ *   q [total_q, Hq, d], k and v [total_k, Hkv, d], o [total_q, Hq, d]: bf16,
+ *     given as attn_tensor with stride_h and stride_n (stride_b is ignored).
+ *   lse: fp32 [Hq][total_q] contiguous (natural log; -inf and O = 0 for a
+ *     row with no visible key).
+ *   cu_seqlens_q, cu_seqlens_k: device int32 [nseq + 1], nondecreasing from
+ *     0 to total_q (total_k): the cumulative lengths.  Values outside
+ *     [0, total] are clamped (never read out of bounds); other malformed
+ *     offsets give unspecified results.
+ *   spec: ATTN_MASK_CAUSAL, ATTN_MASK_WINDOW, ATTN_MOD_SOFTCAP and
+ *     ATTN_MASK_NO_SKIP apply inside each sequence (ATTN_MASK_DOCS is
+ *     rejected).  With Lq queries and Lk keys in a sequence, local query i
+ *     lines up with local key i + Lk - Lq (the last query with the last
+ *     key): causal keeps keys j <= i + Lk - Lq, the window is taken about
+ *     that key.  For Lq = Lk this is the usual square mask.
+ *   workspace: >= attn_fwd_varlen_workspace_size(total_q, total_k) bytes,
+ *     16-byte aligned (the block mask is built there).
+ * Supported: d in {64, 128}; Hq % Hkv == 0.  total_q == 0 is a no-op.
+ * Errors: ATTN_ERR_INVALID, ATTN_ERR_UNSUPPORTED, ATTN_ERR_WORKSPACE,
+ * ATTN_ERR_HIP.
+ */
+size_t attn_fwd_varlen_workspace_size(int total_q, int total_k);
+attn_status attn_fwd_varlen(attn_tensor q, attn_tensor k, attn_tensor v, attn_tensor o,
+                            float *lse, const int32_t *cu_seqlens_q,
+                            const int32_t *cu_seqlens_k, int nseq, int total_q, int total_k,
+                            int Hq, int Hkv, int d, const attn_mask_spec *spec, float scale,
+                            void *workspace, size_t ws_bytes, void *stream);
+
+/*
  * Split-KV decode: one new query per (batch row, query head) against the
  * first lens[b] keys of a KV cache (aegloslab "3.7 어텐션 II", section
  * 3.7.4).  The valid keys are cut into chunks of `chunk` keys; every

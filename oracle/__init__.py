@@ -5,8 +5,9 @@ Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
 
 The arithmetic lives in ``oracle.c`` (plain fp64 C, OpenMP over rows); this
 module compiles it with gcc when no build is present and marshals numpy
-arrays of bf16 bit patterns (uint16) into it.  Nothing here is shared with
-the HIP library.
+arrays of bf16 bit patterns (uint16) into it.  The packed variable-length
+forward (``fwd_varlen``) is written here in numpy fp64, from the definition.
+Nothing here is shared with the HIP library.
 """
 from __future__ import annotations
 
@@ -194,4 +195,76 @@ def decode(q, kc, vc, lens, *, scale):
                            _ptr(lse))
     if rc != 0:
         raise ValueError("oracle_decode rejected its arguments")
+    return o, lse
+
+
+def _bf16_to_f64(bits):
+    return (np.asarray(bits, dtype=np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def fwd_varlen(q, k, v, cu_q, cu_k, *, scale, causal=False, window=None, softcap=None,
+               rows=None):
+    """Exact attention over packed variable-length sequences, fp64, from the
+    definition (aegloslab "3.7 어텐션 II", section 3.7.6, the varlen form).
+
+    q [total_q, Hq, d], k/v [total_k, Hkv, d]: uint16 bf16 bit patterns.
+    cu_q, cu_k: int [nseq + 1] cumulative lengths.  Sequence s: queries
+    [cu_q[s], cu_q[s+1]), keys [cu_k[s], cu_k[s+1]).  Local query i of a
+    sequence with Lq queries and Lk keys lines up with local key
+    i + Lk - Lq; causal keeps keys j <= i + Lk - Lq, a window (int w or pair
+    (left, right)) keeps i + Lk - Lq - left <= j <= i + Lk - Lq + right.
+    The score is scale * q.k, masked keys are dropped, and the soft cap
+    c * tanh(s / c) applies to the rest.
+    rows: None for every row, else int array [n, 2] of (h, i).
+    Returns (O, LSE): [total_q, Hq, d] and [Hq, total_q], or [n, d] and [n]
+    for selected rows.  A row with no visible key has O = 0, LSE = -inf.
+    """
+    tq, Hq, d = q.shape
+    Hkv = k.shape[1]
+    group = Hq // Hkv
+    cu_q = np.asarray(cu_q, dtype=np.int64)
+    cu_k = np.asarray(cu_k, dtype=np.int64)
+    if window is None:
+        wl = wr = None
+    elif np.isscalar(window):
+        wl = wr = int(window)
+    else:
+        wl, wr = (int(x) for x in window)
+    seq_of = np.searchsorted(cu_q, np.arange(tq), side="right") - 1
+
+    def one_row(h, i):
+        s = int(seq_of[i])
+        q0, q1, k0, k1 = cu_q[s], cu_q[s + 1], cu_k[s], cu_k[s + 1]
+        diag = (i - q0) + (k1 - k0) - (q1 - q0)
+        j = np.arange(k1 - k0)
+        vis = np.ones(j.shape, dtype=bool)
+        if causal:
+            vis &= j <= diag
+        if wl is not None:
+            vis &= (j >= diag - wl) & (j <= diag + wr)
+        if not vis.any():
+            return np.zeros(d), -np.inf
+        hk = h // group
+        kk = _bf16_to_f64(k[k0:k1, hk, :])[vis]
+        vv = _bf16_to_f64(v[k0:k1, hk, :])[vis]
+        sc = (kk @ _bf16_to_f64(q[i, h, :])) * scale
+        if softcap is not None:
+            sc = softcap * np.tanh(sc / softcap)
+        m = sc.max()
+        e = np.exp(sc - m)
+        den = e.sum()
+        return (e / den) @ vv, m + np.log(den)
+
+    if rows is not None:
+        rows = np.asarray(rows, dtype=np.int64).reshape(-1, 2)
+        o = np.empty((rows.shape[0], d))
+        lse = np.empty(rows.shape[0])
+        for n, (h, i) in enumerate(rows):
+            o[n], lse[n] = one_row(int(h), int(i))
+        return o, lse
+    o = np.empty((tq, Hq, d))
+    lse = np.empty((Hq, tq))
+    for h in range(Hq):
+        for i in range(tq):
+            o[i, h], lse[h, i] = one_row(h, i)
     return o, lse

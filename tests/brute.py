@@ -84,3 +84,60 @@ def attention(q, k, v, scale, causal=False, window=None, doc_offsets=None,
         O.append(Ob)
         L.append(Lb)
     return O, L
+
+
+def attention_varlen(q, k, v, cu_q, cu_k, scale, causal=False, window=None, softcap=None):
+    """Packed variable-length attention by loops.  q [tq][Hq][d], k/v
+    [tk][Hkv][d] nested lists of floats; cu_q, cu_k cumulative lengths.
+    Query i of a sequence (local index) sees local key j when
+    j <= i + Lk - Lq (causal) and |j - (i + Lk - Lq)| is inside the window.
+
+    Returns O [tq][Hq][d], LSE [Hq][tq]."""
+    tq, Hq, d = len(q), len(q[0]) if q else 0, len(q[0][0]) if q else 0
+    Hkv = len(k[0]) if k else 1
+    group = Hq // Hkv if Hkv else 1
+    if window is None:
+        wl = wr = None
+    elif isinstance(window, int):
+        wl = wr = window
+    else:
+        wl, wr = window
+    O = [[None] * Hq for _ in range(tq)]
+    L = [[None] * tq for _ in range(Hq)]
+    for s in range(len(cu_q) - 1):
+        lq, lk = cu_q[s + 1] - cu_q[s], cu_k[s + 1] - cu_k[s]
+        for il in range(lq):
+            i = cu_q[s] + il
+            shift = il + lk - lq
+            for h in range(Hq):
+                hk = h // group
+                scores = []
+                for jl in range(lk):
+                    if causal and jl > shift:
+                        continue
+                    if wl is not None and not (shift - wl <= jl <= shift + wr):
+                        continue
+                    j = cu_k[s] + jl
+                    dot = 0.0
+                    for t in range(d):
+                        dot += q[i][h][t] * k[j][hk][t]
+                    sc = dot * scale
+                    if softcap is not None:
+                        sc = softcap * math.tanh(sc / softcap)
+                    scores.append((j, sc))
+                if not scores:
+                    O[i][h] = [0.0] * d
+                    L[h][i] = -math.inf
+                    continue
+                mx = max(sc for _, sc in scores)
+                den = 0.0
+                for _, sc in scores:
+                    den += math.exp(sc - mx)
+                out = [0.0] * d
+                for j, sc in scores:
+                    w = math.exp(sc - mx) / den
+                    for t in range(d):
+                        out[t] += w * v[j][hk][t]
+                O[i][h] = out
+                L[h][i] = mx + math.log(den)
+    return O, L

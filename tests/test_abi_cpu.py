@@ -32,6 +32,7 @@ def test_header_declares_the_boundary():
     for n in ("attn_fwd", "attn_decode", "attn_mask_build", "attn_mask_bytes",
               "attn_fwd_workspace_size", "attn_decode_workspace_size",
               "attn_bwd", "attn_bwd_workspace_size",
+              "attn_fwd_varlen", "attn_fwd_varlen_workspace_size",
               "attn_status_string", "attn_last_error"):
         assert n in names
 
@@ -154,3 +155,36 @@ def test_bwd_validation_before_launch(lib):
     assert call(ws=ctypes.c_void_p(16), ws_bytes=64) == b.ATTN_ERR_WORKSPACE
     assert call(B=0) == b.ATTN_OK
     assert call(N=0) == b.ATTN_OK
+
+
+def test_varlen_validation_before_launch(lib):
+    from exact_attention_15_amd import binding as b
+    t = _t(16, 0, 0, 256)
+    lse = ctypes.c_void_p(16)
+
+    def call(d=128, Hq=4, Hkv=2, nseq=2, tq=10, tk=12, cu_q=16, cu_k=16, flags=0, ws=None,
+             ws_bytes=0, kt=t):
+        spec = b.AttnMaskSpec(flags, 0, 0, 0.0, None, 0)
+        return lib.attn_fwd_varlen(t, kt, kt, t, lse, cu_q, cu_k, nseq, tq, tk, Hq, Hkv, d,
+                                   ctypes.byref(spec), ctypes.c_float(0.1), ws, ws_bytes, None)
+    assert call(d=96) == b.ATTN_ERR_UNSUPPORTED
+    assert call(Hq=3, Hkv=2) == b.ATTN_ERR_INVALID
+    assert call(nseq=-1) == b.ATTN_ERR_INVALID
+    assert call(nseq=0) == b.ATTN_ERR_INVALID            # rows but no sequence
+    assert call(cu_q=None) == b.ATTN_ERR_INVALID
+    assert call(flags=b.ATTN_MASK_DOCS) == b.ATTN_ERR_INVALID
+    assert call() == b.ATTN_ERR_WORKSPACE
+    assert call(tq=0) == b.ATTN_OK                         # nothing to do
+    # with no keys, k and v are never read and may be null
+    assert call(tk=0, kt=_t(0, 0, 0, 0)) == b.ATTN_ERR_WORKSPACE
+
+
+def test_varlen_workspace_size(lib):
+    # the block mask of one batch row: total_q rows over total_k keys
+    def a256(x):
+        return (x + 255) & ~255
+    for tq, tk in [(10, 12), (5000, 300), (300, 5000)]:
+        nqt, nkt = (tq + 127) // 128, (tk + 63) // 64
+        want = 2 * a256(4 * tq) + 2 * a256(4 * nqt) + a256(4 * nqt * nkt)
+        assert lib.attn_fwd_varlen_workspace_size(tq, tk) == want
+    assert lib.attn_fwd_varlen_workspace_size(0, 10) == 0
