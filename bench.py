@@ -20,12 +20,15 @@ The same JSON line also carries:
   varlen        attn_fwd_varlen on the GQA document workload packed into
                 [B*N, H, d] with its documents as the sequences (config 7,
                 run with config 4);
+  alibi         the forward kernel on the headline workload with the ALiBi
+                distance bias, slopes 2^(-8(h+1)/H) (config 8, run with
+                config 2);
   configs       every workload's time and throughput;
   cpu_baseline  the fp64 oracle timed on the host cores on a bounded sample
                 of the headline workload (rows of a few heads).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-                       [--configs 1,2,3,4,5,6,7]
+                       [--configs 1,2,3,4,5,6,7,8]
 """
 from __future__ import annotations
 
@@ -387,7 +390,7 @@ def main(argv=None):
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--configs", default="1,2,3,4,5,6,7")
+    ap.add_argument("--configs", default="1,2,3,4,5,6,7,8")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run one device-to-device copy of MIB MiB (a known-size "
@@ -419,8 +422,9 @@ def main(argv=None):
     results = {}
     headline = None
     varlen_res = None
+    alibi_res = None
     for cid in cfg_ids:
-        if cid in (5, 6, 7):
+        if cid in (5, 6, 7, 8):
             continue
         print(f"[bench] config {cid}: generating inputs", file=sys.stderr, flush=True)
         w = fwd_workload(cid, dev)
@@ -453,6 +457,26 @@ def main(argv=None):
             results[varlen_res["workload"]] = {"ms": varlen_res["ms"], "tflops": varlen_res["tflops"]}
             print(f"[bench] config 7 (config 4 packed, varlen): {rv['ms']:.3f} ms, "
                   f"{rv['tflops']:.1f} TFLOP/s", file=sys.stderr, flush=True)
+        if cid == 2 and 8 in cfg_ids:
+            # the same workload with the ALiBi distance bias (geometric slopes)
+            import torch as _t
+            slopes = _t.tensor([2.0 ** (-8.0 * (h + 1) / c["Hq"]) for h in range(c["Hq"])],
+                               dtype=_t.float32, device=dev)
+            wa = dict(w, kw_dev=dict(w["kw_dev"], alibi_slopes=slopes))
+            ra = bench_fwd(ea, wa, args.steps, args.warmup)
+            alibi_res = {
+                "workload": "alibi_" + c["name"], "slopes": "2^(-8(h+1)/H)",
+                "ms_step": round(ra["ms_step"], 4), "ms_kernel": round(ra["ms_kernel"], 4),
+                "tflops_kernel": round(ra["tflops_kernel"], 2),
+                "roofline": {"bound": "mfma", "achieved": round(ra["tflops_kernel"], 2),
+                             "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                             "frac": round(ra["tflops_kernel"] / MFMA_BF16_PEAK_TFLOPS, 4),
+                             "traffic": None, "kernel": "k_attn_fwd_d128_alibi"},
+            }
+            results[alibi_res["workload"]] = {"ms_kernel": alibi_res["ms_kernel"],
+                                              "tflops_kernel": alibi_res["tflops_kernel"]}
+            print(f"[bench] config 8 (config 2 with ALiBi): {ra['ms_kernel']:.3f} ms kernel, "
+                  f"{ra['tflops_kernel']:.1f} TFLOP/s", file=sys.stderr, flush=True)
         if cid == 2:
             headline = (w, r)
         else:
@@ -535,6 +559,8 @@ def main(argv=None):
         out["backward"] = bwd_res
     if varlen_res is not None:
         out["varlen"] = varlen_res
+    if alibi_res is not None:
+        out["alibi"] = alibi_res
     out["configs"] = results
     print(json.dumps(out), flush=True)
     return 0

@@ -23,6 +23,7 @@ ATTN_MASK_WINDOW = 2
 ATTN_MASK_DOCS = 4
 ATTN_MOD_SOFTCAP = 8
 ATTN_MASK_NO_SKIP = 16
+ATTN_MOD_ALIBI = 32
 
 # Tile sizes of the forward kernel (block-mask granularity).
 BLOCK_M = 128
@@ -37,7 +38,8 @@ class AttnTensor(ctypes.Structure):
 class AttnMaskSpec(ctypes.Structure):
     _fields_ = [("flags", ctypes.c_uint32), ("window_left", ctypes.c_int32),
                 ("window_right", ctypes.c_int32), ("softcap", ctypes.c_float),
-                ("doc_offsets", ctypes.c_void_p), ("doc_stride", ctypes.c_int32)]
+                ("doc_offsets", ctypes.c_void_p), ("doc_stride", ctypes.c_int32),
+                ("alibi_slopes", ctypes.c_void_p)]
 
 
 class AttnError(RuntimeError):
@@ -121,7 +123,7 @@ class MaskSpec:
     """Python holder of an ``attn_mask_spec`` (keeps doc_offsets alive)."""
 
     def __init__(self, *, causal=False, window=None, doc_offsets=None,
-                 softcap=None, no_skip=False):
+                 softcap=None, no_skip=False, alibi_slopes=None):
         flags = 0
         wl = wr = 0
         if causal:
@@ -143,7 +145,15 @@ class MaskSpec:
             cap = float(softcap)
         if no_skip:
             flags |= ATTN_MASK_NO_SKIP
-        self.c = AttnMaskSpec(flags, int(wl), int(wr), cap, doc_ptr, doc_stride)
+        self.alibi_slopes = None
+        slopes_ptr = None
+        if alibi_slopes is not None:
+            if alibi_slopes.dtype != torch.float32 or not alibi_slopes.is_cuda or alibi_slopes.dim() != 1:
+                raise TypeError("alibi_slopes: expected a float32 [Hq] GPU tensor")
+            flags |= ATTN_MOD_ALIBI
+            self.alibi_slopes = alibi_slopes.contiguous()
+            slopes_ptr = self.alibi_slopes.data_ptr()
+        self.c = AttnMaskSpec(flags, int(wl), int(wr), cap, doc_ptr, doc_stride, slopes_ptr)
 
     def ref(self):
         return ctypes.byref(self.c)
@@ -160,7 +170,8 @@ def mask_build(spec: MaskSpec, B: int, N: int, device=None) -> torch.Tensor:
 
 
 def fwd(q, k, v, *, causal=False, window=None, doc_offsets=None, softcap=None,
-        scale=None, block_mask=None, no_skip=False, spec=None, out=None, lse=None):
+        scale=None, block_mask=None, no_skip=False, spec=None, out=None, lse=None,
+        alibi_slopes=None):
     """Exact attention forward.  q [B,Hq,N,d], k/v [B,Hkv,N,d] bf16 (any
     batch/head/token strides).  Returns (O [B,Hq,N,d] bf16, LSE [B,Hq,N] fp32)."""
     lib = _load()
@@ -172,7 +183,9 @@ def fwd(q, k, v, *, causal=False, window=None, doc_offsets=None, softcap=None,
         raise ValueError(f"k/v must be [B, Hkv, N, d]; got {tuple(k.shape)} and {tuple(v.shape)}")
     if spec is None:
         spec = MaskSpec(causal=causal, window=window, doc_offsets=doc_offsets,
-                        softcap=softcap, no_skip=no_skip)
+                        softcap=softcap, no_skip=no_skip, alibi_slopes=alibi_slopes)
+    if spec.alibi_slopes is not None and spec.alibi_slopes.numel() != Hq:
+        raise ValueError("alibi_slopes must hold one slope per query head")
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     if out is None:

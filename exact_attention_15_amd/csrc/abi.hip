@@ -39,8 +39,8 @@ attn_status check_tensor(const attn_tensor &t, const char *name, bool need_n_str
     return ATTN_OK;
 }
 
-const uint32_t KNOWN_FLAGS =
-    ATTN_MASK_CAUSAL | ATTN_MASK_WINDOW | ATTN_MASK_DOCS | ATTN_MOD_SOFTCAP | ATTN_MASK_NO_SKIP;
+const uint32_t KNOWN_FLAGS = ATTN_MASK_CAUSAL | ATTN_MASK_WINDOW | ATTN_MASK_DOCS | ATTN_MOD_SOFTCAP |
+                             ATTN_MASK_NO_SKIP | ATTN_MOD_ALIBI;
 
 attn_status check_spec(const attn_mask_spec *spec) {
     if (!spec) return ATTN_OK;
@@ -53,6 +53,8 @@ attn_status check_spec(const attn_mask_spec *spec) {
         if (!(spec->softcap > 0.f) || !std::isfinite(spec->softcap))
             return fail(ATTN_ERR_INVALID, "mask spec: softcap must be finite and > 0");
     }
+    if ((spec->flags & ATTN_MOD_ALIBI) && !spec->alibi_slopes)
+        return fail(ATTN_ERR_INVALID, "mask spec: ATTN_MOD_ALIBI needs alibi_slopes");
     return ATTN_OK;
 }
 
@@ -64,6 +66,8 @@ void set_score_params(FwdParams &p, const attn_mask_spec &sp, float scale) {
     p.cap_inv_scale_2log2e = softcap ? 2.f * log2e * (scale / sp.softcap) : 0.f;
     p.cap_log2 = softcap ? sp.softcap * log2e : 0.f;
     p.cap_log2_2 = 2.f * p.cap_log2;
+    p.cap_inv2 = softcap ? 2.f / sp.softcap : 0.f;
+    p.alibi_slopes = (sp.flags & ATTN_MOD_ALIBI) ? sp.alibi_slopes : nullptr;
 }
 
 attn_mask_spec spec_or_default(const attn_mask_spec *spec) {
@@ -161,7 +165,7 @@ attn_status attn_fwd(attn_tensor q, attn_tensor k, attn_tensor v, attn_tensor o,
     p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.N = N; p.Nk = N; p.nqt = L.nqt; p.nkt = L.nkt;
     set_score_params(p, sp, scale);
     p.mask = mask_view(mask, L);
-    hipError_t e = launch_fwd(p, d, sp.flags & ATTN_MOD_SOFTCAP, s);
+    hipError_t e = launch_fwd(p, d, sp.flags & ATTN_MOD_SOFTCAP, sp.flags & ATTN_MOD_ALIBI, s);
     if (e != hipSuccess) return hip_fail(e, "attn_fwd");
     return ATTN_OK;
 }
@@ -187,6 +191,8 @@ attn_status attn_fwd_varlen(attn_tensor q, attn_tensor k, attn_tensor v, attn_te
     if (st != ATTN_OK) return st;
     if (spec && (spec->flags & ATTN_MASK_DOCS))
         return fail(ATTN_ERR_INVALID, "attn_fwd_varlen: ATTN_MASK_DOCS does not apply (sequences come from cu_seqlens)");
+    if (spec && (spec->flags & ATTN_MOD_ALIBI))
+        return fail(ATTN_ERR_UNSUPPORTED, "attn_fwd_varlen: ATTN_MOD_ALIBI is supported by attn_fwd only");
     if (total_q == 0) return ATTN_OK;
     if (nseq == 0) return fail(ATTN_ERR_INVALID, "attn_fwd_varlen: total_q=%d rows but no sequence", total_q);
     if (!cu_seqlens_q || !cu_seqlens_k) return fail(ATTN_ERR_INVALID, "attn_fwd_varlen: null cu_seqlens");
@@ -224,7 +230,7 @@ attn_status attn_fwd_varlen(attn_tensor q, attn_tensor k, attn_tensor v, attn_te
     p.B = 1; p.Hq = Hq; p.Hkv = Hkv; p.N = total_q; p.Nk = total_k; p.nqt = L.nqt; p.nkt = L.nkt;
     set_score_params(p, sp, scale);
     p.mask = mask_view(workspace, L);
-    e = launch_fwd(p, d, sp.flags & ATTN_MOD_SOFTCAP, s);
+    e = launch_fwd(p, d, sp.flags & ATTN_MOD_SOFTCAP, false, s);
     if (e != hipSuccess) return hip_fail(e, "attn_fwd_varlen");
     return ATTN_OK;
 }
@@ -247,6 +253,8 @@ attn_status attn_bwd(attn_tensor q, attn_tensor k, attn_tensor v, attn_tensor o,
     if (!std::isfinite(scale) || !(scale > 0.f)) return fail(ATTN_ERR_INVALID, "attn_bwd: scale must be finite and > 0");
     attn_status st = check_spec(spec);
     if (st != ATTN_OK) return st;
+    if (spec && (spec->flags & ATTN_MOD_ALIBI))
+        return fail(ATTN_ERR_UNSUPPORTED, "attn_bwd: ATTN_MOD_ALIBI is supported by attn_fwd only");
     if (int64_t(B) * N == 0) return ATTN_OK;
     const attn_tensor *ts[] = {&q, &k, &v, &o, &dout, &dq, &dk, &dv};
     const char *names[] = {"q", "k", "v", "o", "dout", "dq", "dk", "dv"};

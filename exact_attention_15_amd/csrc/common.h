@@ -86,10 +86,12 @@ struct FwdParams {
     float cap_inv_scale_2log2e; // 2 * log2(e) * scale / c (softcap mode only)
     float cap_log2;             // c * log2(e)     (softcap mode only)
     float cap_log2_2;           // 2 * c * log2(e) (softcap mode only)
+    float cap_inv2;             // 2 / c           (softcap with ALiBi)
+    const float *alibi_slopes;  // [Hq], natural units (ALiBi mode only)
     MaskView mask;
 };
 
-hipError_t launch_fwd(const FwdParams &p, int d, bool softcap, hipStream_t stream);
+hipError_t launch_fwd(const FwdParams &p, int d, bool softcap, bool alibi, hipStream_t stream);
 
 // Backward tiling.  The dQ kernel uses the forward decomposition and block
 // mask.  The dK/dV kernel gives a workgroup BWD_KB keys (4 waves x 32) and

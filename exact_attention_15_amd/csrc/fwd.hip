@@ -32,6 +32,10 @@
 //
 // Scores are kept in base-2 units (scale * log2 e folded into one FMA), so
 // every exponential is one v_exp_f32.
+//
+// ALiBi (a distance bias added before the softmax, aegloslab "3.7 어텐션 II",
+// section 3.7.5) is a compile-time variant: the score becomes
+// scale * q.k - slope_h * |i - j| in base-2 units before the cap and mask.
 #include "tile.h"
 
 namespace exattn {
@@ -50,8 +54,12 @@ extern __shared__ __attribute__((aligned(1024))) uint8_t smem_raw[];
 
 // The kernel body is a device template; the __global__ entry points below
 // are plain (non-template) functions, one per head dim and score mod.
-template <int D, bool SOFTCAP>
+template <int D, bool SOFTCAP, bool ALIBI>
 __device__ __forceinline__ void attn_fwd_body(const FwdParams &p) {
+    // Without the cap or the bias, raw dot products are kept until the
+    // exponent's FMA applies the scale; otherwise scores are formed in
+    // base-2 units first.
+    constexpr bool SCALED = SOFTCAP || ALIBI;
     using C = FwdCfg<D>;
     lds_u8 *smem = (lds_u8 *)(smem_raw); // generic -> LDS address space
 
@@ -107,6 +115,10 @@ __device__ __forceinline__ void attn_fwd_body(const FwdParams &p) {
         lo = p.mask.lo[int64_t(b) * p.N + row];
         hi = p.mask.hi[int64_t(b) * p.N + row];
     }
+
+    // ALiBi slope of this query head, base-2 units
+    float slope = 0.f;
+    if constexpr (ALIBI) slope = p.alibi_slopes[h] * 1.4426950408889634f;
 
     const int ntiles = __builtin_amdgcn_readfirstlane(p.mask.count[item]);
     const int32_t *tiles = p.mask.list + int64_t(item) * p.nkt;
@@ -241,10 +253,32 @@ __device__ __forceinline__ void attn_fwd_body(const FwdParams &p) {
             t[r] = s0[r];
             t[16 + r] = s1[r];
         }
+        if constexpr (ALIBI) {
+            // key - row for register j is rel + c_j, c_j = 32 * (j / 16) +
+            // acc_row(j % 16, 0); the bias -slope * |key - row| is
+            // -|y| (slope >= 0) or +|y| with y = slope * (key - row), one FMA
+            // each, the absolute value being an operand modifier
+            const float srel = slope * float(kt * BLOCK_N + 4 * half - row);
+            if (slope >= 0.f) {
+#pragma unroll
+                for (int j = 0; j < 32; ++j) {
+                    const float y = __builtin_fmaf(float(32 * (j >> 4) + acc_row(j & 15, 0)), slope, srel);
+                    t[j] = __builtin_fmaf(t[j], p.scale_log2, -fabsf(y));
+                }
+            } else {
+#pragma unroll
+                for (int j = 0; j < 32; ++j) {
+                    const float y = __builtin_fmaf(float(32 * (j >> 4) + acc_row(j & 15, 0)), slope, srel);
+                    t[j] = __builtin_fmaf(t[j], p.scale_log2, fabsf(y));
+                }
+            }
+        }
         if constexpr (SOFTCAP) {
+            // with the bias the score is already scaled (base-2 units)
+            const float k2 = ALIBI ? p.cap_inv2 : p.cap_inv_scale_2log2e;
 #pragma unroll
             for (int j = 0; j < 32; ++j) {
-                const float e = __builtin_amdgcn_exp2f(t[j] * p.cap_inv_scale_2log2e);
+                const float e = __builtin_amdgcn_exp2f(t[j] * k2);
                 t[j] = p.cap_log2 - p.cap_log2_2 * __builtin_amdgcn_rcpf(e + 1.f);
             }
         }
@@ -268,7 +302,7 @@ __device__ __forceinline__ void attn_fwd_body(const FwdParams &p) {
             for (int k = 0; k < 4; ++k) mx[k] = fmaxf(mx[k], t[i + k]);
         float mt = fmaxf(fmaxf(mx[0], mx[1]), fmaxf(mx[2], mx[3]));
         mt = fmaxf(mt, wave_swap_halves(mt, half));
-        if constexpr (!SOFTCAP) mt *= p.scale_log2;
+        if constexpr (!SCALED) mt *= p.scale_log2;
         // Rescale O and l only when some valid row's max grew by more than
         // RESCALE_LOG2 (a wave-uniform decision); otherwise keep the older,
         // smaller reference max: p stays <= 2^RESCALE_LOG2 and the result is
@@ -287,7 +321,7 @@ __device__ __forceinline__ void attn_fwd_body(const FwdParams &p) {
         float ps[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int j = 0; j < 32; ++j) {
-            if constexpr (SOFTCAP)
+            if constexpr (SCALED)
                 t[j] = __builtin_amdgcn_exp2f(t[j] - m_use);
             else
                 t[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(t[j], p.scale_log2, -m_use));
@@ -379,12 +413,16 @@ __device__ __forceinline__ void attn_fwd_body(const FwdParams &p) {
     }
 }
 
-#define EXATTN_FWD_KERNEL(NAME, D, SOFTCAP)                                                    \
-    __global__ __launch_bounds__(256, 2) void NAME(FwdParams p) { attn_fwd_body<D, SOFTCAP>(p); }
-EXATTN_FWD_KERNEL(k_attn_fwd_d128, 128, false)
-EXATTN_FWD_KERNEL(k_attn_fwd_d128_softcap, 128, true)
-EXATTN_FWD_KERNEL(k_attn_fwd_d64, 64, false)
-EXATTN_FWD_KERNEL(k_attn_fwd_d64_softcap, 64, true)
+#define EXATTN_FWD_KERNEL(NAME, D, SOFTCAP, ALIBI)                                             \
+    __global__ __launch_bounds__(256, 2) void NAME(FwdParams p) { attn_fwd_body<D, SOFTCAP, ALIBI>(p); }
+EXATTN_FWD_KERNEL(k_attn_fwd_d128, 128, false, false)
+EXATTN_FWD_KERNEL(k_attn_fwd_d128_softcap, 128, true, false)
+EXATTN_FWD_KERNEL(k_attn_fwd_d64, 64, false, false)
+EXATTN_FWD_KERNEL(k_attn_fwd_d64_softcap, 64, true, false)
+EXATTN_FWD_KERNEL(k_attn_fwd_d128_alibi, 128, false, true)
+EXATTN_FWD_KERNEL(k_attn_fwd_d128_softcap_alibi, 128, true, true)
+EXATTN_FWD_KERNEL(k_attn_fwd_d64_alibi, 64, false, true)
+EXATTN_FWD_KERNEL(k_attn_fwd_d64_softcap_alibi, 64, true, true)
 #undef EXATTN_FWD_KERNEL
 
 static hipError_t launch_kernel(void (*kernel)(FwdParams), size_t lds_bytes, const FwdParams &p,
@@ -398,10 +436,15 @@ static hipError_t launch_kernel(void (*kernel)(FwdParams), size_t lds_bytes, con
     return hipGetLastError();
 }
 
-hipError_t launch_fwd(const FwdParams &p, int d, bool softcap, hipStream_t stream) {
+hipError_t launch_fwd(const FwdParams &p, int d, bool softcap, bool alibi, hipStream_t stream) {
+    void (*kernel)(FwdParams);
     if (d == 128)
-        return launch_kernel(softcap ? k_attn_fwd_d128_softcap : k_attn_fwd_d128, FwdCfg<128>::LDS_BYTES, p, stream);
-    return launch_kernel(softcap ? k_attn_fwd_d64_softcap : k_attn_fwd_d64, FwdCfg<64>::LDS_BYTES, p, stream);
+        kernel = alibi ? (softcap ? k_attn_fwd_d128_softcap_alibi : k_attn_fwd_d128_alibi)
+                       : (softcap ? k_attn_fwd_d128_softcap : k_attn_fwd_d128);
+    else
+        kernel = alibi ? (softcap ? k_attn_fwd_d64_softcap_alibi : k_attn_fwd_d64_alibi)
+                       : (softcap ? k_attn_fwd_d64_softcap : k_attn_fwd_d64);
+    return launch_kernel(kernel, d == 128 ? FwdCfg<128>::LDS_BYTES : FwdCfg<64>::LDS_BYTES, p, stream);
 }
 
 static_assert(FwdCfg<128>::LOADS == 4 && FwdCfg<64>::LOADS == 2, "tile loads per wave");

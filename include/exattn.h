@@ -56,15 +56,21 @@ enum {
     ATTN_MASK_WINDOW = 2u,  /* visible only if i - window_left <= j <= i + window_right */
     ATTN_MASK_DOCS = 4u,    /* visible only inside the query's document */
     ATTN_MOD_SOFTCAP = 8u,  /* visible scores s -> softcap * tanh(s / softcap) */
-    ATTN_MASK_NO_SKIP = 16u /* diagnostic: visit every key tile (none skipped,
-                               all element-masked); results are bitwise equal */
+    ATTN_MASK_NO_SKIP = 16u, /* diagnostic: visit every key tile (none skipped,
+                                all element-masked); results are bitwise equal */
+    ATTN_MOD_ALIBI = 32u     /* distance bias: s -> s - slope[h] * |i - j| (attn_fwd only) */
 };
 
 /*
  * Mask specification.  Every supported mask gives each query row one
  * contiguous interval of visible keys, which is what the block mask stores.
- * The scaled score is masked to -inf first; the soft cap then applies to the
- * remaining scores only, so masked keys get weight exactly 0.
+ * The scaled score gets the ALiBi bias (if any), is masked to -inf, and the
+ * soft cap then applies to the remaining scores only, so masked keys get
+ * weight exactly 0.  ALiBi adds a distance-based bias before the softmax
+ * (aegloslab "3.7 어텐션 II", section 3.7.5): query head h subtracts
+ * alibi_slopes[h] * |i - j|; the slopes are the caller's (the usual choice
+ * is a geometric sequence over the heads).  It does not change which tiles
+ * the block mask skips.
  */
 typedef struct {
     uint32_t flags;
@@ -75,6 +81,7 @@ typedef struct {
                                    row 0 = o_0 < o_1 < ... < o_n = N, padded with N
                                    (cumulative document boundaries) */
     int32_t doc_stride;         /* entries per batch row (max documents + 1), >= 2 */
+    const float *alibi_slopes;  /* ATTN_MOD_ALIBI: device fp32 [Hq], finite */
 } attn_mask_spec;
 
 /* A strided bf16 tensor view: element (b, h, n, t) lives at
@@ -147,7 +154,7 @@ attn_status attn_fwd(attn_tensor q, attn_tensor k, attn_tensor v, attn_tensor o,
  *     offsets give unspecified results.
  *   spec: ATTN_MASK_CAUSAL, ATTN_MASK_WINDOW, ATTN_MOD_SOFTCAP and
  *     ATTN_MASK_NO_SKIP apply inside each sequence (ATTN_MASK_DOCS is
- *     rejected).  With Lq queries and Lk keys in a sequence, local query i
+ *     rejected, ATTN_MOD_ALIBI unsupported).  With Lq queries and Lk keys in a sequence, local query i
  *     lines up with local key i + Lk - Lq (the last query with the last
  *     key): causal keeps keys j <= i + Lk - Lq, the window is taken about
  *     that key.  For Lq = Lk this is the usual square mask.
@@ -208,8 +215,9 @@ attn_status attn_decode(attn_tensor q, attn_tensor k_cache, attn_tensor v_cache,
  *   workspace: >= attn_bwd_workspace_size(spec, B, Hq, N) bytes, 16-byte
  *     aligned (the call builds its block masks and per-row data there).
  *   q, k, v, o and dout token strides must be below 2^24 elements.
- * Supported: d in {64, 128}; Hq % Hkv == 0.  Errors: ATTN_ERR_INVALID,
- * ATTN_ERR_UNSUPPORTED, ATTN_ERR_WORKSPACE, ATTN_ERR_HIP.
+ * Supported: d in {64, 128}; Hq % Hkv == 0; not ATTN_MOD_ALIBI
+ * (ATTN_ERR_UNSUPPORTED).  Errors: ATTN_ERR_INVALID, ATTN_ERR_UNSUPPORTED,
+ * ATTN_ERR_WORKSPACE, ATTN_ERR_HIP.
  */
 size_t attn_bwd_workspace_size(const attn_mask_spec *spec, int B, int Hq, int N);
 attn_status attn_bwd(attn_tensor q, attn_tensor k, attn_tensor v, attn_tensor o,

@@ -17,7 +17,7 @@ import subprocess
 
 import numpy as np
 
-CAUSAL, WINDOW, DOCS, SOFTCAP = 1, 2, 4, 8
+CAUSAL, WINDOW, DOCS, SOFTCAP, ALIBI = 1, 2, 4, 8, 16
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
@@ -45,7 +45,7 @@ def _load():
         lib.oracle_fwd.restype = i32
         lib.oracle_fwd.argtypes = [P, P, P, P, P, P, i32, i32, i32, i32, i32,
                                    i32, i64, i64, f64, P, i32, f64, i64, P, P,
-                                   P, P]
+                                   P, P, P]
         lib.oracle_decode.restype = i32
         lib.oracle_decode.argtypes = [P, P, P, P, P, P, i32, i32, i32, i32,
                                       i32, f64, P, P]
@@ -74,12 +74,13 @@ def _strides(a: np.ndarray) -> np.ndarray:
 
 
 def fwd(q, k, v, *, scale, causal=False, window=None, doc_offsets=None,
-        softcap=None, rows=None, want_probs=False):
+        softcap=None, alibi_slopes=None, rows=None, want_probs=False):
     """Exact attention, fp64.
 
     q [B,Hq,N,d], k/v [B,Hkv,N,d]: uint16 bf16 bit patterns.
     window: None, an int w (|i-j| <= w) or a pair (left, right).
     doc_offsets: int32 [B][max_docs+1] padded with N, or None.
+    alibi_slopes: None or [Hq] floats: score -= slope[h] * |i - j|.
     rows: None for every row, else int array [n,3] of (b, h, i).
     Returns (O [..., d] float64, LSE float64[, P]) shaped [B,Hq,N,...] for
     all rows, or [n, ...] for selected rows.
@@ -107,6 +108,12 @@ def fwd(q, k, v, *, scale, causal=False, window=None, doc_offsets=None,
     if softcap is not None:
         flags |= SOFTCAP
         cap = float(softcap)
+    slopes = None
+    if alibi_slopes is not None:
+        flags |= ALIBI
+        slopes = np.ascontiguousarray(alibi_slopes, dtype=np.float64)
+        if slopes.shape != (Hq,):
+            raise ValueError("alibi_slopes must hold one slope per query head")
     if rows is None:
         nrows = B * Hq * N
         rows_arr = None
@@ -120,7 +127,7 @@ def fwd(q, k, v, *, scale, causal=False, window=None, doc_offsets=None,
     rc = lib.oracle_fwd(_ptr(q), _ptr(qs), _ptr(k), _ptr(ks), _ptr(v), _ptr(vs),
                         B, Hq, Hkv, N, d, flags, int(wl), int(wr), cap,
                         _ptr(offs), doc_stride, float(scale), nrows,
-                        _ptr(rows_arr), _ptr(o), _ptr(lse), _ptr(p))
+                        _ptr(rows_arr), _ptr(o), _ptr(lse), _ptr(p), _ptr(slopes))
     if rc != 0:
         raise ValueError("oracle_fwd rejected its arguments")
     if rows is None:

@@ -14,17 +14,21 @@
  *      the dense definition (mdooai.com "어텐션 최적화: FlashAttention과 희소
  *      어텐션", the key-formula section; the -inf convention for keys outside
  *      the allowed set is the sparse-attention formula of the same page);
- *   2. the soft cap, on visible scores only: S <- c * tanh(S / c) (a kernel
- *      flag in aegloslab "3.7 어텐션 II" section 3.7.5; the order scale ->
- *      mask -> cap is the reading stated in the design notes);
- *   3. the row softmax P_ij = exp(S_ij - m_i) / sum_j exp(S_ij - m_i) with
+ *   2. with the ALiBi flag, a distance bias on visible scores:
+ *      S <- S - slope_h * |i - j| for query head h (a bias added before the
+ *      softmax that grows with the query-key distance, aegloslab "3.7
+ *      어텐션 II" section 3.7.5; the per-head slopes are an input);
+ *   3. the soft cap, on visible scores only: S <- c * tanh(S / c) (a kernel
+ *      flag in the same section; the order scale -> bias -> mask -> cap is
+ *      the reading stated in the design notes);
+ *   4. the row softmax P_ij = exp(S_ij - m_i) / sum_j exp(S_ij - m_i) with
  *      m_i = max_j S_ij (llm-systems-engineering "Attention 최적화가 어려운
  *      이유", sections on the computation flow and on the remaining scores);
- *   4. O_i = sum_j P_ij v_j and LSE_i = m_i + ln sum_j exp(S_ij - m_i), the
+ *   5. O_i = sum_j P_ij v_j and LSE_i = m_i + ln sum_j exp(S_ij - m_i), the
  *      natural-log form of the row statistics m and l that the forward pass
  *      keeps for the backward pass (youngju.dev "FlashAttention 논문 분석",
  *      section "Recomputation 전략").
- *   5. A row with no visible key gives O_i = 0 and LSE_i = -inf.
+ *   6. A row with no visible key gives O_i = 0 and LSE_i = -inf.
  *
  * Visibility of key j for query i in batch row b:
  *   CAUSAL : j <= i
@@ -51,6 +55,7 @@
 #define ORACLE_WINDOW 2
 #define ORACLE_DOCS 4
 #define ORACLE_SOFTCAP 8
+#define ORACLE_ALIBI 16
 
 static double widen_bf16(uint16_t bits)
 {
@@ -70,6 +75,7 @@ typedef struct {
     const int32_t *doc_offsets; /* [B][doc_stride], padded with N */
     int doc_stride;
     double scale;
+    const double *alibi_slopes; /* [Hq], with ORACLE_ALIBI */
 } fwd_problem;
 
 /* Index of the document holding token i: the number of interior boundaries
@@ -148,6 +154,8 @@ static void fwd_row(const fwd_problem *p, int b, int h, int i, double *srow,
         for (t = 0; t < p->d; ++t)
             dot += widen_bf16(qi[t]) * widen_bf16(kj[t]);
         double sc = p->scale * dot;
+        if (p->flags & ORACLE_ALIBI)
+            sc -= p->alibi_slopes[h] * fabs((double)i - (double)j);
         if (p->flags & ORACLE_SOFTCAP)
             sc = p->softcap * tanh(sc / p->softcap);
         srow[j] = sc;
@@ -176,7 +184,7 @@ int oracle_fwd(const uint16_t *q, const int64_t *q_strides, const uint16_t *k,
                int flags, int64_t window_left, int64_t window_right,
                double softcap, const int32_t *doc_offsets, int doc_stride,
                double scale, int64_t nrows, const int32_t *rows, double *out_o,
-               double *out_lse, double *out_p)
+               double *out_lse, double *out_p, const double *alibi_slopes)
 {
     fwd_problem p;
     int64_t total = (int64_t)B * Hq * N;
@@ -186,8 +194,11 @@ int oracle_fwd(const uint16_t *q, const int64_t *q_strides, const uint16_t *k,
         return -1;
     if ((flags & ORACLE_SOFTCAP) && !(softcap > 0.0))
         return -1;
+    if ((flags & ORACLE_ALIBI) && !alibi_slopes)
+        return -1;
     if (!rows)
         nrows = total;
+    p.alibi_slopes = alibi_slopes;
     p.q = q; p.k = k; p.v = v;
     p.qs = q_strides; p.ks = k_strides; p.vs = v_strides;
     p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.N = N; p.d = d;
@@ -301,6 +312,9 @@ int oracle_bwd(const uint16_t *q, const int64_t *q_strides, const uint16_t *k,
     p.flags = flags; p.wl = window_left; p.wr = window_right;
     p.softcap = softcap; p.doc_offsets = doc_offsets; p.doc_stride = doc_stride;
     p.scale = scale;
+    p.alibi_slopes = NULL;
+    if (flags & ORACLE_ALIBI)
+        return -1; /* the gradient oracle covers the forward without the bias */
     memset(out_dq, 0, sizeof(double) * (size_t)B * Hq * N * d);
     memset(out_dk, 0, sizeof(double) * (size_t)B * Hkv * N * d);
     memset(out_dv, 0, sizeof(double) * (size_t)B * Hkv * N * d);

@@ -24,8 +24,9 @@ def doc_ids_from_offsets(offsets, N):
 
 
 def attention(q, k, v, scale, causal=False, window=None, doc_offsets=None,
-              softcap=None):
-    """q [B][Hq][N][d], k/v [B][Hkv][N][d] nested lists of floats.
+              softcap=None, alibi_slopes=None):
+    """q [B][Hq][N][d], k/v [B][Hkv][N][d] nested lists of floats;
+    alibi_slopes: per query head, the score loses slope * |i - j|.
 
     Returns O [B][Hq][N][d], LSE [B][Hq][N] as nested lists of floats."""
     B, Hq, N, d = len(q), len(q[0]), len(q[0][0]), len(q[0][0][0])
@@ -61,6 +62,8 @@ def attention(q, k, v, scale, causal=False, window=None, doc_offsets=None,
                     for t in range(d):
                         dot += q[b][h][i][t] * k[b][hk][j][t]
                     s = dot * scale
+                    if alibi_slopes is not None:
+                        s -= alibi_slopes[h] * abs(i - j)
                     if softcap is not None:
                         s = softcap * math.tanh(s / softcap)
                     scores.append((j, s))

@@ -188,3 +188,19 @@ def test_varlen_workspace_size(lib):
         want = 2 * a256(4 * tq) + 2 * a256(4 * nqt) + a256(4 * nqt * nkt)
         assert lib.attn_fwd_varlen_workspace_size(tq, tk) == want
     assert lib.attn_fwd_varlen_workspace_size(0, 10) == 0
+
+
+def test_alibi_validation(lib):
+    from exact_attention_15_amd import binding as b
+    t = _t(16, 0, 0, 128)
+    no_slopes = b.AttnMaskSpec(b.ATTN_MOD_ALIBI, 0, 0, 0.0, None, 0, None)
+    st = lib.attn_fwd(t, t, t, t, ctypes.c_void_p(16), 1, 2, 2, 8, 128, ctypes.byref(no_slopes),
+                      ctypes.c_float(0.1), None, None, 0, None)
+    assert st == b.ATTN_ERR_INVALID and b"alibi_slopes" in lib.attn_last_error()
+    spec = b.AttnMaskSpec(b.ATTN_MOD_ALIBI, 0, 0, 0.0, None, 0, 64)
+    st = lib.attn_bwd(t, t, t, t, ctypes.c_void_p(16), t, t, t, t, 1, 2, 2, 8, 128,
+                      ctypes.byref(spec), ctypes.c_float(0.1), None, 0, None)
+    assert st == b.ATTN_ERR_UNSUPPORTED
+    st = lib.attn_fwd_varlen(t, t, t, t, ctypes.c_void_p(16), 16, 16, 1, 8, 8, 2, 2, 128,
+                             ctypes.byref(spec), ctypes.c_float(0.1), None, 0, None)
+    assert st == b.ATTN_ERR_UNSUPPORTED
