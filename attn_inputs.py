@@ -4,7 +4,7 @@ This module is shared by the oracle side (tests, ``bench.py``'s CPU baseline)
 and the HIP side (the binding's tests, ``bench.py``'s timed path).  It holds
 no attention arithmetic: it only draws random numbers, rounds them to bf16
 and builds the integer structure (document offsets, decode lengths) that the
-five workloads need.
+workloads need.
 
 Recipe (the same for every caller):
 
@@ -106,7 +106,7 @@ def draw_decode_lens(rng: np.random.Generator, B: int, lo: int = 1024,
     return rng.integers(lo, hi + 1, size=B).astype(np.int32)
 
 
-# The five workloads.  ``kind`` selects the mask; sizes are the full ones.
+# The workloads.  ``kind`` selects the mask; sizes are the full ones.
 CONFIGS = {
     1: dict(name="causal_b1_h2_n256_d64", kind="causal", B=1, Hq=2, Hkv=2,
             N=256, d=64, factor=1.0, seed=1001),
@@ -123,6 +123,10 @@ CONFIGS = {
     # backward of workload 2: its Q, K, V and a seeded output gradient dO
     6: dict(name="bwd_causal_b8_h32_n4096_d128", kind="causal", B=8, Hq=32, Hkv=32,
             N=4096, d=128, factor=0.5, seed=1002, dout_seed=1006),
+    # workload 2 in FP8: Q and K rotated by the same random-sign Hadamard
+    # matrix, all three block-quantized to E4M3 (V with one scale per head)
+    9: dict(name="fp8_causal_b8_h32_n4096_d128", kind="causal", B=8, Hq=32, Hkv=32,
+            N=4096, d=128, factor=0.5, seed=1002, signs_seed=1009),
 }
 
 
@@ -150,6 +154,13 @@ def decode_inputs(seed: int, B: int, Hq: int, Hkv: int, T: int, d: int,
     vc = draw_bf16(rng, (B, Hkv, T, d), factor)
     lens = draw_decode_lens(rng, B, lens_lo, lens_hi)
     return q, kc, vc, lens
+
+
+def hadamard_signs(seed: int, d: int = 128) -> np.ndarray:
+    """Random +-1 signs (int8 [d]) of the rotation used before FP8
+    quantization."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    return rng.choice([-1, 1], size=d).astype(np.int8)
 
 
 def dout_input(seed: int, B: int, Hq: int, N: int, d: int) -> np.ndarray:

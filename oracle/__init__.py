@@ -275,3 +275,112 @@ def fwd_varlen(q, k, v, cu_q, cu_k, *, scale, causal=False, window=None, softcap
         for i in range(tq):
             o[i, h], lse[h, i] = one_row(h, i)
     return o, lse
+
+
+# ---------------------------------------------------------------------------
+# FP8 (E4M3) block quantization with incoherent processing (youngju.dev
+# "FlashAttention 논문 분석", FlashAttention-3 section "FP8 지원과 정확도
+# 유지": a scale per block, and a random orthogonal matrix applied to Q and K
+# before quantization).
+# ---------------------------------------------------------------------------
+E4M3_MAX = 448.0
+
+
+def e4m3_decode(codes):
+    """E4M3 (OCP FP8, bias 7, no infinities, S.1111.111 = NaN) -> float64."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = (c & 7).astype(np.float64)
+    val = np.where(e == 0, m * 2.0 ** -9, (1.0 + m / 8.0) * np.exp2(e - 7.0))
+    val = np.where((e == 15) & (m == 7), np.nan, val)
+    return sign * val
+
+
+def e4m3_encode(x):
+    """Round-to-nearest-even E4M3 codes of finite values with |x| <= 448."""
+    x = np.asarray(x, dtype=np.float64)
+    if not np.all(np.isfinite(x)) or np.any(np.abs(x) > E4M3_MAX):
+        raise ValueError("e4m3_encode: values must be finite with |x| <= 448")
+    a = np.abs(x)
+    sign = np.where(np.signbit(x), 0x80, 0)
+    with np.errstate(divide="ignore"):
+        e = np.floor(np.log2(np.where(a > 0, a, 1.0))).astype(np.int64)
+    # subnormals (a < 2^-6): multiples of 2^-9
+    sub = a < 2.0 ** -6
+    msub = np.rint(a / 2.0 ** -9).astype(np.int64)  # 0..8; 8 is the smallest normal
+    # normals: (1 + m/8) 2^e, with the mantissa rounded to 3 bits
+    e = np.clip(e, -6, 8)
+    frac = a / np.exp2(e.astype(np.float64))  # in [1, 2) up to the log2 rounding
+    lo = frac < 1.0
+    e = np.where(lo, e - 1, e)
+    frac = np.where(lo, frac * 2.0, frac)
+    hi = frac >= 2.0
+    e = np.where(hi, e + 1, e)
+    frac = np.where(hi, frac / 2.0, frac)
+    m = np.rint((frac - 1.0) * 8.0).astype(np.int64)  # 0..8
+    carry = m == 8
+    e = np.where(carry, e + 1, e)
+    m = np.where(carry, 0, m)
+    normal = ((e + 7) << 3) | m
+    code = np.where(sub, msub, normal)  # msub == 8 encodes as exponent 1, mantissa 0
+    return (code | sign).astype(np.uint8)
+
+
+def hadamard_rotate(y, signs):
+    """Rows of y (float32, last axis d, a power of two) times
+    diag(signs) H / sqrt(d), H the Walsh-Hadamard matrix, in float32 with the
+    radix-2 butterfly: for stride h = 1, 2, ..., d/2 the element with the
+    stride bit clear becomes a + b and its partner a - b."""
+    y = np.asarray(y, dtype=np.float32) * np.asarray(signs, dtype=np.float32)
+    d = y.shape[-1]
+    h = 1
+    while h < d:
+        z = y.reshape(y.shape[:-1] + (d // (2 * h), 2, h))
+        a, b = z[..., 0, :].copy(), z[..., 1, :].copy()
+        z[..., 0, :] = a + b
+        z[..., 1, :] = a - b
+        y = z.reshape(y.shape)
+        h *= 2
+    return (y * np.float32(1.0 / np.sqrt(d))).astype(np.float32)
+
+
+def quantize_fp8(x_bits, *, signs=None, per_head=False, block=64):
+    """E4M3 codes [B,H,N,d] and power-of-two scales float32 [B,H,ceil(N/block)]
+    of a bf16 tensor: every `block` rows of a (b, h) (or the whole head) get
+    the scale 2^e, e the smallest integer with max|block| <= 448 * 2^e
+    (2^0 for an all-zero block), and the codes are RNE(x / 2^e).  With signs
+    the rows are first rotated by diag(signs) H / sqrt(d) in float32."""
+    x = (np.asarray(x_bits, dtype=np.uint32) << 16).view(np.float32)
+    B, H, N, d = x.shape
+    y = hadamard_rotate(x, signs) if signs is not None else x.astype(np.float32)
+    nblk = (N + block - 1) // block
+    amax = np.zeros((B, H, nblk), dtype=np.float64)
+    for i in range(nblk):
+        amax[:, :, i] = np.abs(y[:, :, i * block:(i + 1) * block]).max(axis=(2, 3))
+    if per_head:
+        amax[:] = amax.max(axis=2, keepdims=True)
+    e = np.zeros(amax.shape, dtype=np.int64)
+    pos = amax > 0
+    e[pos] = np.ceil(np.log2(amax[pos] / E4M3_MAX)).astype(np.int64)
+    # settle the boundary exactly: smallest e with amax <= 448 * 2^e
+    e = np.where(pos & (amax <= E4M3_MAX * np.exp2(e - 1.0)), e - 1, e)
+    e = np.where(pos & (amax > E4M3_MAX * np.exp2(e.astype(np.float64))), e + 1, e)
+    scales = np.exp2(e.astype(np.float64)).astype(np.float32)
+    rows_scale = np.repeat(scales, block, axis=2)[:, :, :N, None].astype(np.float64)
+    codes = e4m3_encode(y.astype(np.float64) / rows_scale)
+    return codes, scales
+
+
+def dequantize_fp8(codes, scales, block=64):
+    """bf16 bit patterns of codes * scale (exact: E4M3 values times powers of
+    two are bf16 values)."""
+    N = codes.shape[2]
+    v = e4m3_decode(codes) * np.repeat(scales.astype(np.float64), block, axis=2)[:, :, :N, None]
+    f = v.astype(np.float32)
+    if not np.array_equal(f.astype(np.float64), v):
+        raise ValueError("dequantized value not representable")
+    bits = f.view(np.uint32)
+    if np.any(bits & 0xFFFF):
+        raise ValueError("dequantized value not a bf16 value")
+    return (bits >> 16).astype(np.uint16)
