@@ -23,12 +23,16 @@ The same JSON line also carries:
   alibi         the forward kernel on the headline workload with the ALiBi
                 distance bias, slopes 2^(-8(h+1)/H) (config 8, run with
                 config 2);
+  fp8           the FP8 forward kernel on the headline workload's inputs,
+                Q and K rotated by a random-sign Hadamard matrix and all
+                three block-quantized to E4M3 (config 9): TFLOP/s against
+                the fp8 dense MFMA peak, plus the quantization time;
   configs       every workload's time and throughput;
   cpu_baseline  the fp64 oracle timed on the host cores on a bounded sample
                 of the headline workload (rows of a few heads).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-                       [--configs 1,2,3,4,5,6,7,8]
+                       [--configs 1,2,3,4,5,6,7,8,9]
 """
 from __future__ import annotations
 
@@ -49,6 +53,7 @@ import attn_inputs as gen  # noqa: E402
 
 METRIC = "fwd attention TFLOPS & % bf16 MFMA peak; decode split-KV HBM GB/s"
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
+MFMA_FP8_PEAK_TFLOPS = 5000.0   # MI355X dense fp8
 HBM_PEAK_GBS = 8000.0           # MI355X HBM3E
 # Backward FLOPs: five products per visible pair (S recomputed, dP, dV, dK,
 # dQ), 2*d each, against the forward's two.
@@ -353,6 +358,43 @@ def bench_varlen(ea, w, steps, warmup):
     return dict(ms=ms, nseq=len(cu) - 1, tflops=w["flops"] / (ms * 1e-3) / 1e12)
 
 
+def bench_fp8(ea, w, steps, warmup):
+    """Quantization (three attn_quantize_fp8 calls: Q and K rotated, V with
+    one scale per head) and the FP8 forward kernel with a prebuilt block
+    mask, on the forward workload ``w``."""
+    import torch
+    c = w["cfg"]
+    B, Hq, N, d = c["B"], c["Hq"], c["N"], c["d"]
+    dev = w["q"].device
+    signs = torch.from_numpy(gen.hadamard_signs(c["signs_seed"], d)).to(dev)
+    spec = ea.MaskSpec(**w["kw_dev"])
+    q8, qs = ea.quantize_fp8(w["q"], signs=signs)
+    k8, ks = ea.quantize_fp8(w["k"], signs=signs)
+    v8, vs = ea.quantize_fp8(w["v"], per_head=True)
+    o = torch.empty((B, Hq, N, d), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((B, Hq, N), dtype=torch.float32, device=dev)
+    bm = ea.mask_build(spec, B, N)
+
+    def quantize():
+        ea.quantize_fp8(w["q"], signs=signs, out=q8, scales=qs)
+        ea.quantize_fp8(w["k"], signs=signs, out=k8, scales=ks)
+        ea.quantize_fp8(w["v"], per_head=True, out=v8, scales=vs)
+
+    def kernel_only():
+        ea.fwd_fp8(q8, k8, v8, qs, ks, vs, spec=spec, scale=w["scale"], block_mask=bm, out=o, lse=lse)
+
+    warm_gpu(kernel_only)
+    ms_kernel = time_launches(kernel_only, steps, warmup)
+    dist = time_each(kernel_only, max(steps, 20))
+    ms_quant = time_launches(quantize, max(steps // 2, 5), 2)
+    # HBM bytes of the three quantize calls: bf16 in twice (max pass and
+    # apply pass), codes out once
+    qbytes = 3 * B * Hq * N * d * (2 * 2 + 1)
+    return dict(ms_kernel=ms_kernel, dist=dist, ms_quant=ms_quant,
+                tflops_kernel=w["flops"] / (ms_kernel * 1e-3) / 1e12,
+                quant_gbs=qbytes / (ms_quant * 1e-3) / 1e9)
+
+
 def cpu_baseline(w, target_s=15.0):
     """The fp64 oracle on whole (batch row, head) slices of the workload, timed
     on the host cores; throughput in the metric's unit (TFLOP/s).  One slice
@@ -390,7 +432,7 @@ def main(argv=None):
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--configs", default="1,2,3,4,5,6,7,8")
+    ap.add_argument("--configs", default="1,2,3,4,5,6,7,8,9")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run one device-to-device copy of MIB MiB (a known-size "
@@ -423,8 +465,9 @@ def main(argv=None):
     headline = None
     varlen_res = None
     alibi_res = None
+    fp8_res = None
     for cid in cfg_ids:
-        if cid in (5, 6, 7, 8):
+        if cid in (5, 6, 7, 8, 9):
             continue
         print(f"[bench] config {cid}: generating inputs", file=sys.stderr, flush=True)
         w = fwd_workload(cid, dev)
@@ -477,6 +520,26 @@ def main(argv=None):
                                               "tflops_kernel": alibi_res["tflops_kernel"]}
             print(f"[bench] config 8 (config 2 with ALiBi): {ra['ms_kernel']:.3f} ms kernel, "
                   f"{ra['tflops_kernel']:.1f} TFLOP/s", file=sys.stderr, flush=True)
+        if cid == 2 and 9 in cfg_ids:
+            rf = bench_fp8(ea, dict(w, cfg=gen.CONFIGS[9]), args.steps, args.warmup)
+            fp8_res = {
+                "workload": gen.CONFIGS[9]["name"],
+                "rotation": "diag(random signs) * Hadamard / sqrt(128) on Q and K",
+                "ms_kernel": round(rf["ms_kernel"], 4),
+                "kernel_median_ms": round(rf["dist"]["median_ms"], 4),
+                "tflops_kernel": round(rf["tflops_kernel"], 2),
+                "ms_quantize_qkv": round(rf["ms_quant"], 4),
+                "quantize_gbs": round(rf["quant_gbs"], 1),
+                "roofline": {"bound": "mfma", "achieved": round(rf["tflops_kernel"], 2),
+                             "peak": MFMA_FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
+                             "frac": round(rf["tflops_kernel"] / MFMA_FP8_PEAK_TFLOPS, 4),
+                             "traffic": None, "kernel": "k_attn_fwd8_d128"},
+            }
+            results[fp8_res["workload"]] = {"ms_kernel": fp8_res["ms_kernel"],
+                                            "tflops_kernel": fp8_res["tflops_kernel"]}
+            print(f"[bench] config 9 (config 2 in FP8): {rf['ms_kernel']:.3f} ms kernel, "
+                  f"{rf['tflops_kernel']:.1f} TFLOP/s; quantize {rf['ms_quant']:.3f} ms",
+                  file=sys.stderr, flush=True)
         if cid == 2:
             headline = (w, r)
         else:
@@ -561,6 +624,8 @@ def main(argv=None):
         out["varlen"] = varlen_res
     if alibi_res is not None:
         out["alibi"] = alibi_res
+    if fp8_res is not None:
+        out["fp8"] = fp8_res
     out["configs"] = results
     print(json.dumps(out), flush=True)
     return 0

@@ -74,6 +74,12 @@ def _load():
     lib.attn_fwd_varlen_workspace_size.argtypes = [i32, i32]
     lib.attn_fwd_varlen.restype = i32
     lib.attn_fwd_varlen.argtypes = [T, T, T, T, P, P, P, i32, i32, i32, i32, i32, i32, SP, f32, P, sz, P]
+    lib.attn_quantize_fp8_workspace_size.restype = sz
+    lib.attn_quantize_fp8_workspace_size.argtypes = [i32, i32, i32]
+    lib.attn_quantize_fp8.restype = i32
+    lib.attn_quantize_fp8.argtypes = [T, T, P, i32, i32, i32, i32, P, i32, P, sz, P]
+    lib.attn_fwd_fp8.restype = i32
+    lib.attn_fwd_fp8.argtypes = [T, T, T, P, P, P, T, P, i32, i32, i32, i32, i32, SP, f32, P, P, sz, P]
     lib.attn_decode_workspace_size.restype = sz
     lib.attn_decode_workspace_size.argtypes = [i32, i32, i32, i32, i32]
     lib.attn_decode.restype = i32
@@ -294,6 +300,71 @@ def bwd(q, k, v, o, lse, dout, *, causal=False, window=None, doc_offsets=None,
 
 def bwd_workspace_bytes(B, Hq, N, spec=None) -> int:
     return _load().attn_bwd_workspace_size(None if spec is None else spec.ref(), B, Hq, N)
+
+
+def _tensor4u8(t: torch.Tensor) -> AttnTensor:
+    if t.dim() != 4 or t.dtype != torch.uint8 or not t.is_cuda:
+        raise TypeError("expected a uint8 [B, H, N, d] GPU tensor of E4M3 codes")
+    if t.stride(-1) != 1:
+        raise ValueError("the head dimension must be contiguous")
+    return AttnTensor(t.data_ptr(), t.stride(0), t.stride(1), t.stride(2))
+
+
+def quantize_fp8(x, *, signs=None, per_head=False, out=None, scales=None):
+    """E4M3 block quantization of a bf16 [B, H, N, 128] tensor.  signs: an
+    int8 [128] GPU tensor of +-1 for the random Hadamard rotation (the same
+    for Q and K), or None.  Returns (codes uint8 [B,H,N,128], scales fp32
+    [B, H, ceil(N/64)])."""
+    lib = _load()
+    _check_bf16("x", x)
+    B, H, N, d = x.shape
+    if out is None:
+        out = torch.empty((B, H, N, d), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty((B, H, (N + 63) // 64), dtype=torch.float32, device=x.device)
+    if signs is not None and (signs.dtype != torch.int8 or not signs.is_cuda or signs.numel() != d):
+        raise TypeError("signs: expected an int8 [d] GPU tensor of +-1")
+    ws_bytes = lib.attn_quantize_fp8_workspace_size(B, H, N)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=x.device)
+    st = lib.attn_quantize_fp8(_tensor4(x), _tensor4u8(out), scales.data_ptr(), B, H, N, d,
+                               None if signs is None else signs.data_ptr(), int(bool(per_head)),
+                               ws.data_ptr(), ws_bytes, _stream(x.device))
+    _check(st)
+    return out, scales
+
+
+def fwd_fp8(q8, k8, v8, q_scales, k_scales, v_scales, *, causal=False, window=None,
+            doc_offsets=None, softcap=None, scale=None, block_mask=None, no_skip=False,
+            spec=None, out=None, lse=None):
+    """Forward attention on E4M3 codes from quantize_fp8 (v quantized per
+    head).  Returns (O [B,Hq,N,128] bf16, LSE [B,Hq,N] fp32)."""
+    lib = _load()
+    B, Hq, N, d = q8.shape
+    Hkv = k8.shape[1]
+    if spec is None:
+        spec = MaskSpec(causal=causal, window=window, doc_offsets=doc_offsets, softcap=softcap,
+                        no_skip=no_skip)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty((B, Hq, N, d), dtype=torch.bfloat16, device=q8.device)
+    if lse is None:
+        lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q8.device)
+    for name, t in (("q_scales", q_scales), ("k_scales", k_scales), ("v_scales", v_scales)):
+        if t.dtype != torch.float32 or not t.is_cuda or not t.is_contiguous():
+            raise TypeError(f"{name}: expected a contiguous fp32 GPU tensor")
+    ws = None
+    ws_bytes = 0
+    if block_mask is None:
+        ws_bytes = lib.attn_fwd_workspace_size(spec.ref(), B, N)
+        ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=q8.device)
+    st = lib.attn_fwd_fp8(_tensor4u8(q8), _tensor4u8(k8), _tensor4u8(v8), q_scales.data_ptr(),
+                          k_scales.data_ptr(), v_scales.data_ptr(), _tensor4(out), lse.data_ptr(),
+                          B, Hq, Hkv, N, d, spec.ref(), float(scale),
+                          None if block_mask is None else block_mask.data_ptr(),
+                          None if ws is None else ws.data_ptr(), ws_bytes, _stream(q8.device))
+    _check(st)
+    return out, lse
 
 
 def decode(q, k_cache, v_cache, lens, *, scale=None, chunk=1024, out=None, lse=None,

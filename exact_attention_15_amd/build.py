@@ -10,10 +10,11 @@ CSRC = os.path.join(HERE, "csrc")
 ROOT = os.path.dirname(HERE)
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libexattn.so")
-SOURCES = ["abi.hip", "mask.hip", "fwd.hip", "bwd.hip", "decode.hip"]
+SOURCES = ["abi.hip", "mask.hip", "fwd.hip", "fwd8.hip", "bwd.hip", "decode.hip", "quant.hip"]
 # The forward kernel relies on no NaN semantics (masked scores are -inf), so
 # it drops IEEE NaN quieting: max/min then need no canonicalising moves.
-EXTRA = {"fwd.hip": ["-mno-amdgpu-ieee", "-fno-honor-nans"], "bwd.hip": ["-mno-amdgpu-ieee", "-fno-honor-nans"]}
+EXTRA = {"fwd.hip": ["-mno-amdgpu-ieee", "-fno-honor-nans"], "fwd8.hip": ["-mno-amdgpu-ieee", "-fno-honor-nans"],
+         "bwd.hip": ["-mno-amdgpu-ieee", "-fno-honor-nans"]}
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 FLAGS = [

@@ -319,6 +319,109 @@ attn_status attn_bwd(attn_tensor q, attn_tensor k, attn_tensor v, attn_tensor o,
     return ATTN_OK;
 }
 
+size_t attn_quantize_fp8_workspace_size(int B, int H, int N) {
+    if (B <= 0 || H <= 0 || N <= 0) return 0;
+    return align256(4 * size_t(B) * size_t(H) * size_t((N + 63) / 64));
+}
+
+attn_status attn_quantize_fp8(attn_tensor x, attn_tensor out, float *scales, int B, int H, int N, int d,
+                              const int8_t *signs, int per_head, void *workspace, size_t ws_bytes, void *stream) {
+    if (B < 0 || H <= 0 || N < 0) return fail(ATTN_ERR_INVALID, "attn_quantize_fp8: B=%d H=%d N=%d", B, H, N);
+    if (d != 128) return fail(ATTN_ERR_UNSUPPORTED, "attn_quantize_fp8: head dim %d (supported: 128)", d);
+    if (int64_t(B) * N == 0) return ATTN_OK;
+    attn_status st;
+    if ((st = check_tensor(x, "x", true)) != ATTN_OK) return st;
+    if (!out.ptr || !aligned16(out.ptr)) return fail(ATTN_ERR_INVALID, "attn_quantize_fp8: out null or not 16-byte aligned");
+    if (out.stride_b < 0 || out.stride_h < 0 || out.stride_n < 0 || out.stride_b % 16 || out.stride_h % 16 ||
+        out.stride_n % 16)
+        return fail(ATTN_ERR_INVALID, "attn_quantize_fp8: out strides must be non-negative multiples of 16 bytes");
+    if (!scales) return fail(ATTN_ERR_INVALID, "attn_quantize_fp8: null scales");
+    const size_t need = attn_quantize_fp8_workspace_size(B, H, N);
+    if (!workspace || ws_bytes < need)
+        return fail(ATTN_ERR_WORKSPACE, "attn_quantize_fp8: workspace needs %zu bytes, got %zu", need,
+                    workspace ? ws_bytes : size_t(0));
+    if (int64_t(B) > 65535 || int64_t(H) > 65535)
+        return fail(ATTN_ERR_UNSUPPORTED, "attn_quantize_fp8: B and H must be below 65536");
+    QuantParams p;
+    p.x = static_cast<const uint16_t *>(x.ptr);
+    p.x_sb = x.stride_b; p.x_sh = x.stride_h; p.x_sn = x.stride_n;
+    p.out = static_cast<uint8_t *>(out.ptr);
+    p.o_sb = out.stride_b; p.o_sh = out.stride_h; p.o_sn = out.stride_n;
+    p.scales = scales;
+    p.amax = static_cast<float *>(workspace);
+    p.signs = signs;
+    p.B = B; p.H = H; p.N = N; p.nblk = (N + 63) / 64; p.per_head = per_head ? 1 : 0;
+    p.inv_sqrt_d = float(1.0 / std::sqrt(double(d)));
+    hipError_t e = launch_quant(p, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "attn_quantize_fp8");
+    return ATTN_OK;
+}
+
+attn_status attn_fwd_fp8(attn_tensor q, attn_tensor k, attn_tensor v, const float *q_scales,
+                         const float *k_scales, const float *v_scales, attn_tensor o, float *lse, int B, int Hq,
+                         int Hkv, int N, int d, const attn_mask_spec *spec, float scale, const void *block_mask,
+                         void *workspace, size_t ws_bytes, void *stream) {
+    if (B < 0 || N < 0) return fail(ATTN_ERR_INVALID, "attn_fwd_fp8: B=%d N=%d", B, N);
+    if (Hq <= 0 || Hkv <= 0) return fail(ATTN_ERR_INVALID, "attn_fwd_fp8: Hq=%d Hkv=%d", Hq, Hkv);
+    if (Hq % Hkv) return fail(ATTN_ERR_INVALID, "attn_fwd_fp8: Hq=%d is not a multiple of Hkv=%d", Hq, Hkv);
+    if (d != 128) return fail(ATTN_ERR_UNSUPPORTED, "attn_fwd_fp8: head dim %d (supported: 128)", d);
+    if (!std::isfinite(scale) || !(scale > 0.f)) return fail(ATTN_ERR_INVALID, "attn_fwd_fp8: scale must be finite and > 0");
+    attn_status st = check_spec(spec);
+    if (st != ATTN_OK) return st;
+    if (spec && (spec->flags & ATTN_MOD_ALIBI))
+        return fail(ATTN_ERR_UNSUPPORTED, "attn_fwd_fp8: ATTN_MOD_ALIBI is supported by attn_fwd only");
+    if (int64_t(B) * N == 0) return ATTN_OK;
+    const attn_tensor *ts[] = {&q, &k, &v};
+    const char *names[] = {"q", "k", "v"};
+    for (int i = 0; i < 3; ++i) {
+        const attn_tensor &t = *ts[i];
+        if (!t.ptr || !aligned16(t.ptr)) return fail(ATTN_ERR_INVALID, "attn_fwd_fp8: %s null or not 16-byte aligned", names[i]);
+        if (t.stride_b < 0 || t.stride_h < 0 || t.stride_n < 0 || t.stride_b % 16 || t.stride_h % 16 ||
+            t.stride_n % 16)
+            return fail(ATTN_ERR_INVALID, "attn_fwd_fp8: %s strides must be non-negative multiples of 16 bytes", names[i]);
+        if (t.stride_n >= (int64_t(1) << 24))
+            return fail(ATTN_ERR_UNSUPPORTED, "attn_fwd_fp8: %s token stride must be below 2^24 bytes", names[i]);
+    }
+    if ((st = check_tensor(o, "o", true)) != ATTN_OK) return st;
+    if (!lse || !q_scales || !k_scales || !v_scales) return fail(ATTN_ERR_INVALID, "attn_fwd_fp8: null lse or scales");
+    const MaskLayout L = mask_layout(B, N);
+    if (int64_t(B) * L.nqt * Hq > 0x7FFFFFFFLL) return fail(ATTN_ERR_UNSUPPORTED, "attn_fwd_fp8: grid too large");
+    const attn_mask_spec sp = spec_or_default(spec);
+    const void *mask = block_mask;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (!mask) {
+        if (!workspace || ws_bytes < L.bytes)
+            return fail(ATTN_ERR_WORKSPACE, "attn_fwd_fp8: workspace needs %zu bytes, got %zu", L.bytes,
+                        workspace ? ws_bytes : size_t(0));
+        if (!aligned16(workspace)) return fail(ATTN_ERR_INVALID, "attn_fwd_fp8: workspace not 16-byte aligned");
+        hipError_t e = launch_mask_build(sp, L, workspace, s);
+        if (e != hipSuccess) return hip_fail(e, "attn_fwd_fp8 (mask build)");
+        mask = workspace;
+    }
+    Fwd8Params p;
+    p.q = static_cast<const uint8_t *>(q.ptr);
+    p.k = static_cast<const uint8_t *>(k.ptr);
+    p.v = static_cast<const uint8_t *>(v.ptr);
+    p.o = static_cast<uint16_t *>(o.ptr);
+    p.lse = lse;
+    p.q_scales = q_scales; p.k_scales = k_scales; p.v_scales = v_scales;
+    p.q_sb = q.stride_b; p.q_sh = q.stride_h; p.q_sn = q.stride_n;
+    p.k_sb = k.stride_b; p.k_sh = k.stride_h; p.k_sn = k.stride_n;
+    p.v_sb = v.stride_b; p.v_sh = v.stride_h; p.v_sn = v.stride_n;
+    p.o_sb = o.stride_b; p.o_sh = o.stride_h; p.o_sn = o.stride_n;
+    p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.N = N; p.nqt = L.nqt; p.nkt = L.nkt; p.nblk64 = (N + 63) / 64;
+    const float log2e = 1.4426950408889634f;
+    p.scale_log2 = scale * log2e;
+    const bool softcap = sp.flags & ATTN_MOD_SOFTCAP;
+    p.cap_inv_scale_2log2e = softcap ? 2.f * log2e * (scale / sp.softcap) : 0.f;
+    p.cap_log2 = softcap ? sp.softcap * log2e : 0.f;
+    p.cap_log2_2 = 2.f * p.cap_log2;
+    p.mask = mask_view(mask, L);
+    hipError_t e = launch_fwd8(p, softcap, s);
+    if (e != hipSuccess) return hip_fail(e, "attn_fwd_fp8");
+    return ATTN_OK;
+}
+
 size_t attn_decode_workspace_size(int B, int Hq, int T, int d, int chunk) {
     if (B <= 0 || Hq <= 0 || T < 0 || d <= 0 || chunk <= 0) return 0;
     const int nchunk = T > 0 ? (T + chunk - 1) / chunk : 1;

@@ -133,6 +133,40 @@ struct BwdParams {
 hipError_t launch_bwd(const BwdParams &p, int d, bool softcap, uint32_t flags, const MaskLayout &L,
                       const BwdMaskLayout &BL, void *kv_mask, hipStream_t stream);
 
+// FP8 (E4M3) block quantization of a bf16 [B, H, N, d] tensor (d = 128):
+// codes [B, H, N, d] bytes, scales fp32 [B][H][nblk] (powers of two, one per
+// 64-row block; all equal within a head when per_head is set).
+struct QuantParams {
+    const uint16_t *x;
+    int64_t x_sb, x_sh, x_sn;
+    uint8_t *out;
+    int64_t o_sb, o_sh, o_sn;
+    float *scales;
+    float *amax;         // workspace [B][H][nblk]
+    const int8_t *signs; // [d] of +-1 for the rotation, or null
+    int B, H, N, nblk, per_head;
+    float inv_sqrt_d;
+};
+hipError_t launch_quant(const QuantParams &p, hipStream_t stream);
+
+// FP8 forward (d = 128): q, k, v are E4M3 codes with per-64-row-block
+// scales for q and k and one scale per (b, KV head) for v.
+struct Fwd8Params {
+    const uint8_t *q, *k, *v;
+    uint16_t *o;
+    float *lse;
+    const float *q_scales, *k_scales, *v_scales; // [B][Hq][nblk64], [B][Hkv][nblk64] (v: per head, all equal)
+    int64_t q_sb, q_sh, q_sn;
+    int64_t k_sb, k_sh, k_sn;
+    int64_t v_sb, v_sh, v_sn;
+    int64_t o_sb, o_sh, o_sn;
+    int B, Hq, Hkv, N, nqt, nkt, nblk64;
+    float scale_log2;
+    float cap_inv_scale_2log2e, cap_log2, cap_log2_2; // softcap mode only
+    MaskView mask;
+};
+hipError_t launch_fwd8(const Fwd8Params &p, bool softcap, hipStream_t stream);
+
 struct DecodeParams {
     const uint16_t *q, *k, *v;
     uint16_t *o;

@@ -226,6 +226,48 @@ attn_status attn_bwd(attn_tensor q, attn_tensor k, attn_tensor v, attn_tensor o,
                      const attn_mask_spec *spec, float scale, void *workspace,
                      size_t ws_bytes, void *stream);
 
+/*
+ * FP8 (E4M3) forward, FlashAttention-3's FP8 variant (youngju.dev
+ * "FlashAttention 논문 분석", FlashAttention-3 sections "FP8 텐서 코어" and
+ * "FP8 지원과 정확도 유지"): block quantization and incoherent processing.
+ *
+ * attn_quantize_fp8: E4M3 codes of a bf16 [B,H,N,d] tensor (d = 128).
+ *   Every 64-row block of a (b, h) gets a scale 2^e, the smallest power of
+ *   two with max|block| <= 448 * 2^e (per_head != 0: one scale per (b, h),
+ *   written to each of its blocks); codes are round-to-nearest-even of
+ *   value / 2^e.  With signs (device int8 [d] of +1/-1, the caller's random
+ *   draws) each row is first multiplied by the random orthogonal matrix
+ *   diag(signs) H / sqrt(d), H the Walsh-Hadamard matrix (fast butterfly,
+ *   strides 1, 2, ..., d/2, in fp32): apply the same signs to Q and K (the
+ *   product Q K^T is unchanged) and none to V.
+ *   x: bf16 attn_tensor; out: byte strides (stride_b/h/n in bytes, multiples
+ *   of 16), 16-byte aligned; scales: device fp32 [B][H][ceil(N/64)];
+ *   workspace: >= attn_quantize_fp8_workspace_size(B, H, N) bytes.
+ *
+ * attn_fwd_fp8: attn_fwd on E4M3 inputs (d = 128): S = (q8 . k8) * sq * sk
+ *   * scale with sq, sk the blocks' scales, P rounded to E4M3 (times 256)
+ *   for the P V product, O = sum(P v8) * sv / (256 l) with l the sum of the
+ *   unrounded probabilities.
+ *   q [B,Hq,N,128], k, v [B,Hkv,N,128]: codes from attn_quantize_fp8 (byte
+ *   strides, multiples of 16; token strides below 2^24 bytes);
+ *   q_scales [B][Hq][ceil(N/64)], k_scales and v_scales [B][Hkv][ceil(N/64)]
+ *   device fp32, as written by attn_quantize_fp8; v must be quantized with
+ *   per_head set (its first block's scale is used for the whole head).
+ *   o, lse, spec (not ATTN_MOD_ALIBI), scale, block_mask, workspace: as for
+ *   attn_fwd.
+ * Errors: ATTN_ERR_INVALID, ATTN_ERR_UNSUPPORTED (d != 128, ALiBi),
+ * ATTN_ERR_WORKSPACE, ATTN_ERR_HIP.
+ */
+size_t attn_quantize_fp8_workspace_size(int B, int H, int N);
+attn_status attn_quantize_fp8(attn_tensor x, attn_tensor out, float *scales, int B, int H, int N,
+                              int d, const int8_t *signs, int per_head, void *workspace,
+                              size_t ws_bytes, void *stream);
+attn_status attn_fwd_fp8(attn_tensor q, attn_tensor k, attn_tensor v, const float *q_scales,
+                         const float *k_scales, const float *v_scales, attn_tensor o, float *lse,
+                         int B, int Hq, int Hkv, int N, int d, const attn_mask_spec *spec,
+                         float scale, const void *block_mask, void *workspace, size_t ws_bytes,
+                         void *stream);
+
 /* Static description of a status code. */
 const char *attn_status_string(attn_status status);
 /* Detail for the calling thread's most recent non-OK status ("" if none). */

@@ -33,6 +33,7 @@ def test_header_declares_the_boundary():
               "attn_fwd_workspace_size", "attn_decode_workspace_size",
               "attn_bwd", "attn_bwd_workspace_size",
               "attn_fwd_varlen", "attn_fwd_varlen_workspace_size",
+              "attn_fwd_fp8", "attn_quantize_fp8", "attn_quantize_fp8_workspace_size",
               "attn_status_string", "attn_last_error"):
         assert n in names
 
@@ -204,3 +205,27 @@ def test_alibi_validation(lib):
     st = lib.attn_fwd_varlen(t, t, t, t, ctypes.c_void_p(16), 16, 16, 1, 8, 8, 2, 2, 128,
                              ctypes.byref(spec), ctypes.c_float(0.1), None, 0, None)
     assert st == b.ATTN_ERR_UNSUPPORTED
+
+
+def test_fp8_validation_before_launch(lib):
+    from exact_attention_15_amd import binding as b
+    t = _t(16, 0, 0, 128)
+    f = ctypes.c_void_p(16)
+
+    def fwd8(d=128, Hq=4, Hkv=2, qt=t, flags=0):
+        spec = b.AttnMaskSpec(flags, 0, 0, 0.0, None, 0, 64)
+        return lib.attn_fwd_fp8(qt, t, t, f, f, f, t, f, 1, Hq, Hkv, 8, d, ctypes.byref(spec),
+                                ctypes.c_float(0.1), None, None, 0, None)
+    assert fwd8(d=64) == b.ATTN_ERR_UNSUPPORTED
+    assert fwd8(Hq=3) == b.ATTN_ERR_INVALID
+    assert fwd8(qt=_t(16, 0, 0, 136)) == b.ATTN_ERR_INVALID        # byte strides multiple of 16
+    assert fwd8(flags=b.ATTN_MOD_ALIBI) == b.ATTN_ERR_UNSUPPORTED
+    assert fwd8() == b.ATTN_ERR_WORKSPACE
+
+    def quant(d=128, out=t, scales=16, ws=None, ws_bytes=0):
+        return lib.attn_quantize_fp8(t, out, scales, 1, 2, 100, d, None, 0, ws, ws_bytes, None)
+    assert quant(d=64) == b.ATTN_ERR_UNSUPPORTED
+    assert quant(scales=None) == b.ATTN_ERR_INVALID
+    assert quant(out=_t(16, 0, 0, 8)) == b.ATTN_ERR_INVALID
+    assert quant() == b.ATTN_ERR_WORKSPACE
+    assert lib.attn_quantize_fp8_workspace_size(2, 3, 100) == 256
