@@ -387,9 +387,9 @@ def bench_fp8(ea, w, steps, warmup):
     ms_kernel = time_launches(kernel_only, steps, warmup)
     dist = time_each(kernel_only, max(steps, 20))
     ms_quant = time_launches(quantize, max(steps // 2, 5), 2)
-    # HBM bytes of the three quantize calls: bf16 in twice (max pass and
-    # apply pass), codes out once
-    qbytes = 3 * B * Hq * N * d * (2 * 2 + 1)
+    # algorithmic HBM bytes of the three quantize calls: bf16 in, E4M3 out
+    # (V's per-head scale reads its input twice; that is not counted)
+    qbytes = 3 * B * Hq * N * d * (2 + 1)
     return dict(ms_kernel=ms_kernel, dist=dist, ms_quant=ms_quant,
                 tflops_kernel=w["flops"] / (ms_kernel * 1e-3) / 1e12,
                 quant_gbs=qbytes / (ms_quant * 1e-3) / 1e9)
