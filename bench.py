@@ -71,20 +71,25 @@ MEASURED_TRAFFIC = {
     # kernel: (sources, sha256 of their concatenation, bytes per launch, summary)
     "k_attn_fwd_d128": (
         ["fwd.hip", "tile.h", "common.h"],
-        "47ef7a8c3faa853c52a397c665b9adffad0d42660ca439a3cbed8e98544f6b49",
-        1111661296,
+        "b8a0ba1419009a1e6ed15379c39791f4fef053818c3beb8947ff2391b8f01f1f",
+        1114788987,
         "profiles/k_attn_fwd_d128_causal_b8_h32_n4096_d128.md"),
     "k_decode_split": (
         ["decode.hip", "common.h"],
-        "21063eeaf85f9962e5a5ecb13475022807e8e12c3f10b69c7ecc1fbb1713d46b",
-        958322629,
+        "e9b502f83f34a29df8948325c4c72d65db4ad70c488be7b91fb2e173506e1660",
+        958341818,
         "profiles/k_decode_split_decode_b16_gqa32x8_t32768_d128.md"),
     # all kernels of one attn_bwd call (mask_kv, prep, dQ, dK/dV)
     "attn_bwd_d128": (
         ["bwd.hip", "tile.h", "common.h"],
-        "5619618c6226af9b37d30f53dea4469492ea8e11610d50f81072cdc24275f232",
-        3564192937,
+        "e6e2ffef2557582ebef7dbef7a6222459c4a170353d513e92d4c0933259c3ebe",
+        3563498571,
         "profiles/k_bwd_d128_causal_b8_h32_n4096_d128.md"),
+    "k_attn_fwd8_d128": (
+        ["fwd8.hip", "tile.h", "common.h"],
+        "7f6afec2756c6709cf5afa2292c21ad95d7f4bd62f00aff2352804eff92ab6a3",
+        679398850,
+        "profiles/k_attn_fwd8_d128_causal_b8_h32_n4096_d128.md"),
 }
 
 
@@ -533,7 +538,8 @@ def main(argv=None):
                 "roofline": {"bound": "mfma", "achieved": round(rf["tflops_kernel"], 2),
                              "peak": MFMA_FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
                              "frac": round(rf["tflops_kernel"] / MFMA_FP8_PEAK_TFLOPS, 4),
-                             "traffic": None, "kernel": "k_attn_fwd8_d128"},
+                             "traffic": measured_traffic("k_attn_fwd8_d128"),
+                             "kernel": "k_attn_fwd8_d128"},
             }
             results[fp8_res["workload"]] = {"ms_kernel": fp8_res["ms_kernel"],
                                             "tflops_kernel": fp8_res["tflops_kernel"]}

@@ -310,9 +310,9 @@ __device__ __forceinline__ void attn_fwd_body(const FwdParams &p) {
         // past N never vote, so the decision does not depend on whether
         // fully visible tiles are element-masked.
         const float m_new = fmaxf(m_run, mt);
+        float alpha = 1.f;
         if (__any(row_ok && m_new > m_run + RESCALE_LOG2)) {
-            const float alpha = __builtin_amdgcn_exp2f(m_run - (m_new == -INFINITY ? 0.f : m_new));
-            l_run *= alpha;
+            alpha = __builtin_amdgcn_exp2f(m_run - (m_new == -INFINITY ? 0.f : m_new));
 #pragma unroll
             for (int i = 0; i < C::DBLK; ++i) acc_o[i] *= alpha;
             m_run = m_new;
@@ -327,7 +327,10 @@ __device__ __forceinline__ void attn_fwd_body(const FwdParams &p) {
                 t[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(t[j], p.scale_log2, -m_use));
             ps[j & 3] += t[j];
         }
-        l_run += (ps[0] + ps[1]) + (ps[2] + ps[3]);
+        // one explicit FMA (alpha = 1 without a rescale), so that the sum
+        // rounds the same way in both unrolled copies of the step whatever
+        // the compiler contracts
+        l_run = __builtin_fmaf(l_run, alpha, (ps[0] + ps[1]) + (ps[2] + ps[3]));
 
         // ---- O^T += V^T P^T ----
         u32x4_t pk[4];

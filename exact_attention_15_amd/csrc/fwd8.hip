@@ -261,7 +261,6 @@ __device__ __forceinline__ void attn_fwd8_body(const Fwd8Params &p) {
         if (grow) {
             const float m_new = fmaxf(m_run, mt);
             alpha = __builtin_amdgcn_exp2f(m_run - (m_new == -INFINITY ? 0.f : m_new));
-            l_run *= alpha;
             m_run = m_new;
         }
         // p * 2^(8 - RESCALE8) = 2^(s - m + 8 - RESCALE8) <= 256: the E4M3
@@ -292,7 +291,9 @@ __device__ __forceinline__ void attn_fwd8_body(const Fwd8Params &p) {
                 t[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(t[j], c, -m8));
             ps[j & 3] += t[j];
         }
-        l_run += (ps[0] + ps[1]) + (ps[2] + ps[3]);
+        // one explicit FMA (alpha = 1 without a rescale): the sum rounds the
+        // same way in both unrolled copies of the step
+        l_run = __builtin_fmaf(l_run, alpha, (ps[0] + ps[1]) + (ps[2] + ps[3]));
 
         // ---- P to E4M3, byte b = 16kb + r, then O^T += V^T P^T ----
         i32x8_t pk;

@@ -194,3 +194,69 @@ def test_rotation_lowers_end_to_end_error_with_outliers(ea):
         errs.append(float(np.sqrt(np.mean((bf16_to_f64(o) - ref) ** 2))))
     print(f"[ok] rms error vs bf16 attention: plain {errs[0]:.4f}, rotated {errs[1]:.4f}", flush=True)
     assert errs[1] < errs[0]
+
+
+@pytest.mark.parametrize("N", [1, 65])
+def test_ragged_small_gqa8(ea, N):
+    run_case(ea, B=2, Hq=8, Hkv=1, N=N, seed=1340 + N, causal=True, label=f"fp8 N={N} GQA 8")
+
+
+def test_empty_rows(ea):
+    # keys i+1 .. i+2 only: the last row sees nothing -> O = 0, LSE = -inf
+    run_case(ea, B=1, Hq=2, Hkv=2, N=200, seed=1343, window=(-1, 2), label="fp8 future-only")
+
+
+def test_left_window_documents(ea):
+    rng = np.random.Generator(np.random.PCG64(1344))
+    docs = gen.draw_doc_offsets(rng, 1, 500, 40, 300)
+    run_case(ea, B=1, Hq=4, Hkv=2, N=500, seed=1345, window=(100, 0), docs=docs, label="fp8 left window docs")
+
+
+def _codes(ea, seed, B, Hq, Hkv, N):
+    q, k, v, _ = gen.fwd_inputs(seed, B, Hq, Hkv, N, 128)
+    sg = torch.from_numpy(_signs(seed + 1)).cuda()
+    return (*ea.quantize_fp8(to_dev(q), signs=sg), *ea.quantize_fp8(to_dev(k), signs=sg),
+            *ea.quantize_fp8(to_dev(v), per_head=True))
+
+
+@pytest.mark.parametrize("kind", ["causal", "window", "docs"])
+def test_block_skipping_is_bitwise_neutral(ea, kind):
+    N = 1500
+    Q8, QS, K8, KS, V8, VS = _codes(ea, 1350, 1, 4, 2, N)
+    if kind == "causal":
+        kw = dict(causal=True)
+    elif kind == "window":
+        kw = dict(window=200, softcap=50.0)
+    else:
+        rng = np.random.Generator(np.random.PCG64(1351))
+        padded, _ = gen.pad_offsets(gen.draw_doc_offsets(rng, 1, N, 100, 500), N)
+        kw = dict(causal=True, doc_offsets=torch.from_numpy(padded).cuda())
+    print(f"[case] fp8 skipping neutral {kind}", flush=True)
+    o1, l1 = ea.fwd_fp8(Q8, K8, V8, QS, KS, VS, **kw)
+    o2, l2 = ea.fwd_fp8(Q8, K8, V8, QS, KS, VS, no_skip=True, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_strided_layout_bnhd(ea):
+    # codes stored [B, N, H, 128] and viewed as [B, H, N, 128]: same result
+    Q8, QS, K8, KS, V8, VS = _codes(ea, 1352, 2, 4, 2, 600)
+    t = lambda x: x.transpose(1, 2).contiguous().transpose(1, 2)
+    Q8t, K8t, V8t = t(Q8), t(K8), t(V8)
+    assert Q8t.stride(2) == 4 * 128 and not Q8t.is_contiguous()
+    print("[case] fp8 strided codes", flush=True)
+    o1, l1 = ea.fwd_fp8(Q8, K8, V8, QS, KS, VS, causal=True)
+    out = torch.empty(2, 600, 4, 128, dtype=torch.bfloat16, device="cuda").transpose(1, 2)
+    o2, l2 = ea.fwd_fp8(Q8t, K8t, V8t, QS, KS, VS, causal=True, out=out)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_empty_inputs(ea):
+    # B = 0 and N = 0 are valid calls that do nothing
+    for B, N in ((0, 64), (2, 0)):
+        x = torch.empty(B, 2, N, 128, dtype=torch.bfloat16, device="cuda")
+        codes, scales = ea.quantize_fp8(x)
+        o, lse = ea.fwd_fp8(codes, codes, codes, scales, scales, scales, causal=True)
+        torch.cuda.synchronize()
+        assert o.shape == (B, 2, N, 128) and lse.shape == (B, 2, N)
