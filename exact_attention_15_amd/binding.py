@@ -320,8 +320,13 @@ def quantize_fp8(x, *, signs=None, per_head=False, out=None, scales=None):
     B, H, N, d = x.shape
     if out is None:
         out = torch.empty((B, H, N, d), dtype=torch.uint8, device=x.device)
+    elif tuple(out.shape) != (B, H, N, d):
+        raise ValueError(f"out must be {(B, H, N, d)}; got {tuple(out.shape)}")
     if scales is None:
         scales = torch.empty((B, H, (N + 63) // 64), dtype=torch.float32, device=x.device)
+    elif (tuple(scales.shape) != (B, H, (N + 63) // 64) or scales.dtype != torch.float32
+          or not scales.is_contiguous()):
+        raise ValueError("scales must be a contiguous fp32 [B, H, ceil(N/64)] tensor")
     if signs is not None and (signs.dtype != torch.int8 or not signs.is_cuda or signs.numel() != d):
         raise TypeError("signs: expected an int8 [d] GPU tensor of +-1")
     ws_bytes = lib.attn_quantize_fp8_workspace_size(B, H, N)
@@ -339,8 +344,16 @@ def fwd_fp8(q8, k8, v8, q_scales, k_scales, v_scales, *, causal=False, window=No
     """Forward attention on E4M3 codes from quantize_fp8 (v quantized per
     head).  Returns (O [B,Hq,N,128] bf16, LSE [B,Hq,N] fp32)."""
     lib = _load()
+    for name, t in (("q8", q8), ("k8", k8), ("v8", v8)):
+        _tensor4u8(t)
     B, Hq, N, d = q8.shape
     Hkv = k8.shape[1]
+    if k8.shape != (B, Hkv, N, d) or v8.shape != (B, Hkv, N, d):
+        raise ValueError(f"k8/v8 must be [B, Hkv, N, d]; got {tuple(k8.shape)} and {tuple(v8.shape)}")
+    nblk = (N + 63) // 64
+    for name, t, H in (("q_scales", q_scales, Hq), ("k_scales", k_scales, Hkv), ("v_scales", v_scales, Hkv)):
+        if tuple(t.shape) != (B, H, nblk):
+            raise ValueError(f"{name} must be [B, H, ceil(N/64)] = {(B, H, nblk)}; got {tuple(t.shape)}")
     if spec is None:
         spec = MaskSpec(causal=causal, window=window, doc_offsets=doc_offsets, softcap=softcap,
                         no_skip=no_skip)

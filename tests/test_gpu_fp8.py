@@ -260,3 +260,15 @@ def test_empty_inputs(ea):
         o, lse = ea.fwd_fp8(codes, codes, codes, scales, scales, scales, causal=True)
         torch.cuda.synchronize()
         assert o.shape == (B, 2, N, 128) and lse.shape == (B, 2, N)
+
+
+def test_binding_rejects_bad_shapes(ea):
+    # scale tensors and code tensors are checked before anything is launched
+    Q8, QS, K8, KS, V8, VS = _codes(ea, 1360, 1, 2, 1, 100)
+    with pytest.raises(ValueError):
+        ea.fwd_fp8(Q8, K8, V8, QS[:, :, :1], KS, VS, causal=True)
+    with pytest.raises(ValueError):
+        ea.fwd_fp8(Q8, K8[:, :, :64], V8, QS, KS, VS, causal=True)
+    with pytest.raises(ValueError):
+        ea.quantize_fp8(torch.zeros(1, 2, 100, 128, dtype=torch.bfloat16, device="cuda"),
+                        scales=torch.empty(1, 2, 1, device="cuda"))
