@@ -245,9 +245,11 @@ attn_status attn_bwd(attn_tensor q, attn_tensor k, attn_tensor v, attn_tensor o,
  *   workspace: >= attn_quantize_fp8_workspace_size(B, H, N) bytes.
  *
  * attn_fwd_fp8: attn_fwd on E4M3 inputs (d = 128): S = (q8 . k8) * sq * sk
- *   * scale with sq, sk the blocks' scales, P rounded to E4M3 (times 256)
- *   for the P V product, O = sum(P v8) * sv / (256 l) with l the sum of the
- *   unrounded probabilities.
+ *   * scale with sq, sk the blocks' scales.  For the P V product each
+ *   probability, taken against a reference max that trails the row max by
+ *   at most a factor 4, is rounded to E4M3 as p * 2^6 (<= 256);
+ *   O = sum(p~ v8) * sv / l with l the sum of the unrounded p, and the LSE
+ *   uses the unrounded p as well.
  *   q [B,Hq,N,128], k, v [B,Hkv,N,128]: codes from attn_quantize_fp8 (byte
  *   strides, multiples of 16; token strides below 2^24 bytes);
  *   q_scales [B][Hq][ceil(N/64)], k_scales and v_scales [B][Hkv][ceil(N/64)]
