@@ -67,6 +67,16 @@ void set_score_params(FwdParams &p, const attn_mask_spec &sp, float scale) {
     p.cap_log2 = softcap ? sp.softcap * log2e : 0.f;
     p.cap_log2_2 = 2.f * p.cap_log2;
     p.cap_inv2 = softcap ? 2.f / sp.softcap : 0.f;
+    // tanh(x) = x - x^3/3 + 2x^5/15 - ..., x = scale * raw / c: coefficients
+    // of raw * poly(raw^2), times c * log2(e) * (scale / c)
+    {
+        const double sc = softcap ? double(scale) / double(sp.softcap) : 0.0, k = sc * sc;
+        const double l2 = 1.4426950408889634 * double(scale);
+        p.cap_poly_lim = softcap ? float(0.15 / sc) : 0.f;
+        p.cap_poly[0] = float(l2);
+        p.cap_poly[1] = float(l2 * (-1.0 / 3.0) * k);
+        p.cap_poly[2] = float(l2 * (2.0 / 15.0) * k * k);
+    }
     p.alibi_slopes = (sp.flags & ATTN_MOD_ALIBI) ? sp.alibi_slopes : nullptr;
 }
 

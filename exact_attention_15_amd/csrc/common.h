@@ -87,6 +87,13 @@ struct FwdParams {
     float cap_log2;             // c * log2(e)     (softcap mode only)
     float cap_log2_2;           // 2 * c * log2(e) (softcap mode only)
     float cap_inv2;             // 2 / c           (softcap with ALiBi)
+    // Polynomial form of the cap (softcap mode only): for |raw| <= cap_poly_lim
+    // (|x| <= 0.15 with x = scale * raw / c), c tanh(x) * log2(e) =
+    // raw * (cap_poly[0] + r2 (cap_poly[1] + r2 cap_poly[2])), r2 = raw^2:
+    // tanh's Taylor series to x^5, whose remainder is below 17/315 x^7, a
+    // relative 6.1e-7 at |x| = 0.15.
+    float cap_poly_lim;
+    float cap_poly[3];
     const float *alibi_slopes;  // [Hq], natural units (ALiBi mode only)
     MaskView mask;
 };

@@ -274,12 +274,37 @@ __device__ __forceinline__ void attn_fwd_body(const FwdParams &p) {
             }
         }
         if constexpr (SOFTCAP) {
-            // with the bias the score is already scaled (base-2 units)
-            const float k2 = ALIBI ? p.cap_inv2 : p.cap_inv_scale_2log2e;
+            // Without the bias, a tile whose raw scores all lie in
+            // |scale * s / c| <= 0.15 (a wave-uniform test) takes the
+            // polynomial form of the cap: four VALU operations per score
+            // instead of an exponential, a reciprocal and three more.
+            bool poly = false;
+            if constexpr (!ALIBI) {
+                float am[4];
 #pragma unroll
-            for (int j = 0; j < 32; ++j) {
-                const float e = __builtin_amdgcn_exp2f(t[j] * k2);
-                t[j] = p.cap_log2 - p.cap_log2_2 * __builtin_amdgcn_rcpf(e + 1.f);
+                for (int k = 0; k < 4; ++k) am[k] = fmaxf(fabsf(t[k]), fabsf(t[k + 4]));
+#pragma unroll
+                for (int i = 8; i < 32; i += 4)
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) am[k] = fmaxf(am[k], fabsf(t[i + k]));
+                const float a = fmaxf(fmaxf(am[0], am[1]), fmaxf(am[2], am[3]));
+                poly = __all(a <= p.cap_poly_lim);
+            }
+            if (poly) {
+#pragma unroll
+                for (int j = 0; j < 32; ++j) {
+                    const float r2 = t[j] * t[j];
+                    const float q = __builtin_fmaf(__builtin_fmaf(p.cap_poly[2], r2, p.cap_poly[1]), r2, p.cap_poly[0]);
+                    t[j] *= q;
+                }
+            } else {
+                // with the bias the score is already scaled (base-2 units)
+                const float k2 = ALIBI ? p.cap_inv2 : p.cap_inv_scale_2log2e;
+#pragma unroll
+                for (int j = 0; j < 32; ++j) {
+                    const float e = __builtin_amdgcn_exp2f(t[j] * k2);
+                    t[j] = p.cap_log2 - p.cap_log2_2 * __builtin_amdgcn_rcpf(e + 1.f);
+                }
             }
         }
         if (partial) {

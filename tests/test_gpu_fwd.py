@@ -233,3 +233,26 @@ def test_mask_builder_matches_host(ea, kind, N):
         assert sorted(order[b].tolist()) == list(range(nqt))
         expect_order = sorted(range(nqt), key=lambda x: (-counts[b, x], x))
         assert order[b].tolist() == expect_order
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_softcap_both_forms_in_one_call(ea, d):
+    # Scores of most tiles stay within the range where the kernel uses the
+    # polynomial form of the cap (|scale * s / c| <= 0.15); the query rows
+    # 300..339 are scaled by 12 so that their tiles take the exact form.
+    # Both must match the oracle's libm tanh, including the rows at the
+    # boundary between the two.
+    N, c = 700, 50.0
+    q, k, v, _ = gen.fwd_inputs(40 + d, 1, 2, 2, N, d)
+    qf = gen.f32_from_bf16_bits(q)
+    qf[:, :, 300:340] *= 12.0
+    q = gen.bf16_bits_from_f32(qf)
+    scale = 1.0 / math.sqrt(d)
+    s_big = float(np.abs(np.einsum("hid,hjd->hij", gen.f32_from_bf16_bits(q)[0, :, 300:340].astype(np.float64),
+                                   gen.f32_from_bf16_bits(k)[0].astype(np.float64))).max()) * scale / c
+    assert s_big > 0.15  # the scaled rows leave the polynomial's range
+    print(f"[case] cap50 both forms d={d}, max |scale*s/c| of the scaled rows {s_big:.2f}", flush=True)
+    o, lse = ea.fwd(to_dev(q), to_dev(k), to_dev(v), window=200, softcap=c, scale=scale)
+    torch.cuda.synchronize()
+    ro, rl = oracle.fwd(q, k, v, scale=scale, window=200, softcap=c)
+    compare(bf16_to_f64(o), lse.cpu().numpy(), ro, rl, f"cap50 both forms d={d}")
