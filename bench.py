@@ -71,24 +71,24 @@ MEASURED_TRAFFIC = {
     # kernel: (sources, sha256 of their concatenation, bytes per launch, summary)
     "k_attn_fwd_d128": (
         ["fwd.hip", "tile.h", "common.h"],
-        "b8a0ba1419009a1e6ed15379c39791f4fef053818c3beb8947ff2391b8f01f1f",
-        1114788987,
+        "e76edb2ec1161f94bb1af5be95c3e830153af3fc13d90e08276c5c7db0e1317e",
+        1115790856,
         "profiles/k_attn_fwd_d128_causal_b8_h32_n4096_d128.md"),
     "k_decode_split": (
         ["decode.hip", "common.h"],
-        "e9b502f83f34a29df8948325c4c72d65db4ad70c488be7b91fb2e173506e1660",
-        958341818,
+        "9919d73922911c4971de7ed8345be52bee59d62612c5cb7cd17e6ee4b611eb53",
+        958331723,
         "profiles/k_decode_split_decode_b16_gqa32x8_t32768_d128.md"),
     # all kernels of one attn_bwd call (mask_kv, prep, dQ, dK/dV)
     "attn_bwd_d128": (
         ["bwd.hip", "tile.h", "common.h"],
-        "e6e2ffef2557582ebef7dbef7a6222459c4a170353d513e92d4c0933259c3ebe",
-        3563498571,
+        "8a565bac454c0e417832d1e37bb7fc0f9977daa64385b568e30188ae282a6314",
+        3563480715,
         "profiles/k_bwd_d128_causal_b8_h32_n4096_d128.md"),
     "k_attn_fwd8_d128": (
         ["fwd8.hip", "tile.h", "common.h"],
-        "7f6afec2756c6709cf5afa2292c21ad95d7f4bd62f00aff2352804eff92ab6a3",
-        679398850,
+        "9dfb3a8d0a48d6eda8a8956f5dc8a4866a0226fa4a885179ab2c46a7cc4b4f2e",
+        679395573,
         "profiles/k_attn_fwd8_d128_causal_b8_h32_n4096_d128.md"),
 }
 
