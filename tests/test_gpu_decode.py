@@ -115,3 +115,10 @@ def test_decode_workspace_reuse(ea):
         assert torch.equal(o1, o2) and torch.equal(l1, l2), lens
     run_decode(ea, B=B, Hq=Hq, Hkv=Hkv, T=T, d=d, seed=131, lens=[512, 4999, 3000, 0, 1], chunk=chunk,
                label="reuse oracle")
+
+
+def test_decode_long_cache(ea):
+    # 131072 cached keys: 128 chunk partials per row, so the merge runs over
+    # several batches of chunks; every output is checked
+    run_decode(ea, B=2, Hq=8, Hkv=2, T=131072, d=128, seed=120, lens=[131072, 70001],
+               label="T=131072")

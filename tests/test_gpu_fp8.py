@@ -272,3 +272,34 @@ def test_binding_rejects_bad_shapes(ea):
     with pytest.raises(ValueError):
         ea.quantize_fp8(torch.zeros(1, 2, 100, 128, dtype=torch.bfloat16, device="cuda"),
                         scales=torch.empty(1, 2, 1, device="cuda"))
+
+
+def test_long_sequence_sampled(ea):
+    # 65536 tokens in FP8 (1024 quantization blocks per head), causal,
+    # rotated, on sampled rows
+    from tests.helpers import sample_rows
+    N = 65536
+    q, k, v, _ = gen.fwd_inputs(1370, 1, 2, 2, N, 128)
+    sg = _signs(1371)
+    sgd = torch.from_numpy(sg).cuda()
+    print("[case] fp8 causal N=65536", flush=True)
+    Q8, QS = ea.quantize_fp8(to_dev(q), signs=sgd)
+    K8, KS = ea.quantize_fp8(to_dev(k), signs=sgd)
+    V8, VS = ea.quantize_fp8(to_dev(v), per_head=True)
+    o, lse = ea.fwd_fp8(Q8, K8, V8, QS, KS, VS, causal=True)
+    torch.cuda.synchronize()
+    rng = np.random.Generator(np.random.PCG64(1372))
+    rows = sample_rows(rng, 1, 2, N, 12, must=[(0, 0, 0), (0, 1, N - 1), (0, 0, 32768)])
+    rq = oracle.dequantize_fp8(*oracle.quantize_fp8(q, signs=sg))
+    rk = oracle.dequantize_fp8(*oracle.quantize_fp8(k, signs=sg))
+    rv = oracle.dequantize_fp8(*oracle.quantize_fp8(v, per_head=True))
+    scale = 1.0 / math.sqrt(128)
+    o_np, l_np = bf16_to_f64(o), lse.cpu().numpy()
+    for h in range(2):
+        sel = rows[rows[:, 1] == h]
+        loc = np.stack([np.zeros(len(sel), np.int32), np.zeros(len(sel), np.int32), sel[:, 2]], axis=1)
+        ro, rl, P = oracle.fwd(rq[:, h:h + 1], rk[:, h:h + 1], rv[:, h:h + 1], scale=scale, causal=True,
+                               rows=loc, want_probs=True)
+        va = np.abs(gen.f32_from_bf16_bits(rv[0, h]).astype(np.float64))
+        _check(o_np[0, h, sel[:, 2]], l_np[0, h, sel[:, 2]], ro, rl, P @ va,
+               np.broadcast_to(va.sum(axis=0), (len(sel), 128)), f"fp8 N=65536 h={h}")

@@ -256,3 +256,23 @@ def test_softcap_both_forms_in_one_call(ea, d):
     torch.cuda.synchronize()
     ro, rl = oracle.fwd(q, k, v, scale=scale, window=200, softcap=c)
     compare(bf16_to_f64(o), lse.cpu().numpy(), ro, rl, f"cap50 both forms d={d}")
+
+
+def test_long_sequence_sampled(ea):
+    # 65536 tokens (512 query tiles, tile lists of up to 1024 key tiles),
+    # causal with GQA 2:1, checked on sampled rows including both ends and
+    # the rows around the middle
+    from tests.helpers import sample_rows
+    N = 65536
+    q, k, v, _ = gen.fwd_inputs(45, 1, 2, 1, N, 128)
+    rng = np.random.Generator(np.random.PCG64(46))
+    rows = sample_rows(rng, 1, 2, N, 24, must=[(0, 0, 0), (0, 1, N - 1), (0, 0, 32767), (0, 1, 32768),
+                                               (0, 0, N - 64), (0, 1, 127)])
+    scale = 1.0 / math.sqrt(128)
+    print("[case] causal N=65536 GQA 2:1, sampled rows", flush=True)
+    o, lse = ea.fwd(to_dev(q), to_dev(k), to_dev(v), causal=True, scale=scale)
+    torch.cuda.synchronize()
+    ro, rl = oracle.fwd(q, k, v, scale=scale, causal=True, rows=rows)
+    og = bf16_to_f64(o)[rows[:, 0], rows[:, 1], rows[:, 2]]
+    lg = lse.cpu().numpy()[rows[:, 0], rows[:, 1], rows[:, 2]]
+    compare(og, lg, ro, rl, "causal N=65536")
