@@ -115,6 +115,11 @@ __device__ __forceinline__ void attn_fwd_body(const FwdParams &p) {
         lo = p.mask.lo[int64_t(b) * p.N + row];
         hi = p.mask.hi[int64_t(b) * p.N + row];
     }
+    // Element mask of PARTIAL tiles: the width of the row's interval, and an
+    // offset that puts every key outside it for a row with none (lo > hi;
+    // keys and N stay below 2^30)
+    const uint32_t vis_w = hi >= lo ? uint32_t(hi - lo) : 0u;
+    const uint32_t vis_pad = hi >= lo ? 0u : 0x40000000u;
 
     // ALiBi slope of this query head, base-2 units
     float slope = 0.f;
@@ -308,12 +313,12 @@ __device__ __forceinline__ void attn_fwd_body(const FwdParams &p) {
             }
         }
         if (partial) {
-            const int kb0 = kt * BLOCK_N;
+            // key = kb0 + 4*half + off_j is visible iff key - lo <= hi - lo
+            // as unsigned numbers: one add, one compare and one select
+            const uint32_t nl = uint32_t(kt * BLOCK_N + 4 * half - lo) + vis_pad;
 #pragma unroll
-            for (int j = 0; j < 32; ++j) {
-                const int key = kb0 + 32 * (j >> 4) + acc_row(j & 15, half);
-                if (key < lo || key > hi) t[j] = -INFINITY;
-            }
+            for (int j = 0; j < 32; ++j)
+                if (uint32_t(32 * (j >> 4) + acc_row(j & 15, 0)) + nl > vis_w) t[j] = -INFINITY;
         }
 
         // ---- online softmax ----

@@ -105,6 +105,11 @@ __device__ __forceinline__ void attn_fwd8_body(const Fwd8Params &p) {
         hi = p.mask.hi[int64_t(b) * p.N + row];
         qscale = p.q_scales[(int64_t(b) * p.Hq + h) * p.nblk64 + row / BLOCK_N];
     }
+    // Element mask of PARTIAL tiles: the width of the row's interval, and an
+    // offset that puts every key outside it for a row with none (lo > hi;
+    // keys and N stay below 2^30)
+    const uint32_t vis_w = hi >= lo ? uint32_t(hi - lo) : 0u;
+    const uint32_t vis_pad = hi >= lo ? 0u : 0x40000000u;
     // per-lane base-2 factor of the raw dot products, before the key scale
     const float c_row = p.scale_log2 * qscale;
     const float *kscales = p.k_scales + (int64_t(b) * p.Hkv + hk) * p.nblk64;
@@ -234,12 +239,12 @@ __device__ __forceinline__ void attn_fwd8_body(const Fwd8Params &p) {
             }
         }
         if (partial) {
-            const int kb0 = kt * BLOCK_N;
+            // key = kb0 + 4*half + off_j is visible iff key - lo <= hi - lo
+            // as unsigned numbers: one add, one compare and one select
+            const uint32_t nl = uint32_t(kt * BLOCK_N + 4 * half - lo) + vis_pad;
 #pragma unroll
-            for (int j = 0; j < 32; ++j) {
-                const int key = kb0 + 32 * (j >> 4) + acc_row(j & 15, half);
-                if (key < lo || key > hi) t[j] = -INFINITY;
-            }
+            for (int j = 0; j < 32; ++j)
+                if (uint32_t(32 * (j >> 4) + acc_row(j & 15, 0)) + nl > vis_w) t[j] = -INFINITY;
         }
 
         // ---- online softmax; the reference max moves only when a row's max
