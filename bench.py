@@ -71,24 +71,24 @@ MEASURED_TRAFFIC = {
     # kernel: (sources, sha256 of their concatenation, bytes per launch, summary)
     "k_attn_fwd_d128": (
         ["fwd.hip", "tile.h", "common.h"],
-        "e76edb2ec1161f94bb1af5be95c3e830153af3fc13d90e08276c5c7db0e1317e",
-        1115790856,
+        "432176192ba15b9ea9ef0fb2539addbef0684f4b8f0a17c9bab299bde3485917",
+        1118126762,
         "profiles/k_attn_fwd_d128_causal_b8_h32_n4096_d128.md"),
     "k_decode_split": (
         ["decode.hip", "common.h"],
         "9919d73922911c4971de7ed8345be52bee59d62612c5cb7cd17e6ee4b611eb53",
-        958331723,
+        958325877,
         "profiles/k_decode_split_decode_b16_gqa32x8_t32768_d128.md"),
     # all kernels of one attn_bwd call (mask_kv, prep, dQ, dK/dV)
     "attn_bwd_d128": (
         ["bwd.hip", "tile.h", "common.h"],
         "8a565bac454c0e417832d1e37bb7fc0f9977daa64385b568e30188ae282a6314",
-        3563480715,
+        3563426020,
         "profiles/k_bwd_d128_causal_b8_h32_n4096_d128.md"),
     "k_attn_fwd8_d128": (
         ["fwd8.hip", "tile.h", "common.h"],
-        "9dfb3a8d0a48d6eda8a8956f5dc8a4866a0226fa4a885179ab2c46a7cc4b4f2e",
-        679395573,
+        "ef7c0aecb2781218a80f54367d05cae251ac116e2ca3712d5651f3951d738849",
+        679381880,
         "profiles/k_attn_fwd8_d128_causal_b8_h32_n4096_d128.md"),
 }
 
