@@ -39,6 +39,11 @@ attn_status check_tensor(const attn_tensor &t, const char *name, bool need_n_str
     return ATTN_OK;
 }
 
+// Longest sequence the forward kernels index (keys and rows stay below 2^30
+// so that the element mask's unsigned interval test cannot wrap); far beyond
+// what fits in one GPU's memory.
+const int MAX_TOKENS = 1 << 30;
+
 const uint32_t KNOWN_FLAGS = ATTN_MASK_CAUSAL | ATTN_MASK_WINDOW | ATTN_MASK_DOCS | ATTN_MOD_SOFTCAP |
                              ATTN_MASK_NO_SKIP | ATTN_MOD_ALIBI;
 
@@ -113,6 +118,7 @@ size_t attn_mask_bytes(const attn_mask_spec *spec, int B, int N) {
 attn_status attn_mask_build(const attn_mask_spec *spec, int B, int N, void *out, size_t bytes,
                             void *stream) {
     if (B < 0 || N < 0) return fail(ATTN_ERR_INVALID, "attn_mask_build: B=%d N=%d", B, N);
+    if (N >= MAX_TOKENS) return fail(ATTN_ERR_UNSUPPORTED, "attn_mask_build: N=%d (supported: below 2^30)", N);
     attn_status st = check_spec(spec);
     if (st != ATTN_OK) return st;
     if (int64_t(B) * N == 0) return ATTN_OK;
@@ -134,6 +140,7 @@ attn_status attn_fwd(attn_tensor q, attn_tensor k, attn_tensor v, attn_tensor o,
                      int Hq, int Hkv, int N, int d, const attn_mask_spec *spec, float scale,
                      const void *block_mask, void *workspace, size_t ws_bytes, void *stream) {
     if (B < 0 || N < 0) return fail(ATTN_ERR_INVALID, "attn_fwd: B=%d N=%d", B, N);
+    if (N >= MAX_TOKENS) return fail(ATTN_ERR_UNSUPPORTED, "attn_fwd: N=%d (supported: below 2^30)", N);
     if (Hq <= 0 || Hkv <= 0) return fail(ATTN_ERR_INVALID, "attn_fwd: Hq=%d Hkv=%d", Hq, Hkv);
     if (Hq % Hkv) return fail(ATTN_ERR_INVALID, "attn_fwd: Hq=%d is not a multiple of Hkv=%d", Hq, Hkv);
     if (d != 64 && d != 128) return fail(ATTN_ERR_UNSUPPORTED, "attn_fwd: head dim %d (supported: 64, 128)", d);
@@ -191,6 +198,9 @@ attn_status attn_fwd_varlen(attn_tensor q, attn_tensor k, attn_tensor v, attn_te
                             void *workspace, size_t ws_bytes, void *stream) {
     if (nseq < 0 || total_q < 0 || total_k < 0)
         return fail(ATTN_ERR_INVALID, "attn_fwd_varlen: nseq=%d total_q=%d total_k=%d", nseq, total_q, total_k);
+    if (total_q >= MAX_TOKENS || total_k >= MAX_TOKENS)
+        return fail(ATTN_ERR_UNSUPPORTED, "attn_fwd_varlen: total_q=%d total_k=%d (supported: below 2^30)", total_q,
+                    total_k);
     if (Hq <= 0 || Hkv <= 0) return fail(ATTN_ERR_INVALID, "attn_fwd_varlen: Hq=%d Hkv=%d", Hq, Hkv);
     if (Hq % Hkv) return fail(ATTN_ERR_INVALID, "attn_fwd_varlen: Hq=%d is not a multiple of Hkv=%d", Hq, Hkv);
     if (d != 64 && d != 128)
@@ -257,6 +267,7 @@ attn_status attn_bwd(attn_tensor q, attn_tensor k, attn_tensor v, attn_tensor o,
                      int N, int d, const attn_mask_spec *spec, float scale, void *workspace, size_t ws_bytes,
                      void *stream) {
     if (B < 0 || N < 0) return fail(ATTN_ERR_INVALID, "attn_bwd: B=%d N=%d", B, N);
+    if (N >= MAX_TOKENS) return fail(ATTN_ERR_UNSUPPORTED, "attn_bwd: N=%d (supported: below 2^30)", N);
     if (Hq <= 0 || Hkv <= 0) return fail(ATTN_ERR_INVALID, "attn_bwd: Hq=%d Hkv=%d", Hq, Hkv);
     if (Hq % Hkv) return fail(ATTN_ERR_INVALID, "attn_bwd: Hq=%d is not a multiple of Hkv=%d", Hq, Hkv);
     if (d != 64 && d != 128) return fail(ATTN_ERR_UNSUPPORTED, "attn_bwd: head dim %d (supported: 64, 128)", d);
@@ -372,6 +383,7 @@ attn_status attn_fwd_fp8(attn_tensor q, attn_tensor k, attn_tensor v, const floa
                          int Hkv, int N, int d, const attn_mask_spec *spec, float scale, const void *block_mask,
                          void *workspace, size_t ws_bytes, void *stream) {
     if (B < 0 || N < 0) return fail(ATTN_ERR_INVALID, "attn_fwd_fp8: B=%d N=%d", B, N);
+    if (N >= MAX_TOKENS) return fail(ATTN_ERR_UNSUPPORTED, "attn_fwd_fp8: N=%d (supported: below 2^30)", N);
     if (Hq <= 0 || Hkv <= 0) return fail(ATTN_ERR_INVALID, "attn_fwd_fp8: Hq=%d Hkv=%d", Hq, Hkv);
     if (Hq % Hkv) return fail(ATTN_ERR_INVALID, "attn_fwd_fp8: Hq=%d is not a multiple of Hkv=%d", Hq, Hkv);
     if (d != 128) return fail(ATTN_ERR_UNSUPPORTED, "attn_fwd_fp8: head dim %d (supported: 128)", d);

@@ -105,8 +105,8 @@ typedef struct {
  *   on `stream`.  Depends only on the spec, B and N (never on heads or data),
  *   so one build serves any number of attn_fwd calls with the same mask.
  *   Errors: ATTN_ERR_INVALID (null spec/out with B*N > 0, B < 0, N < 0, bad
- *   doc_stride, softcap <= 0 with ATTN_MOD_SOFTCAP), ATTN_ERR_WORKSPACE
- *   (bytes too small), ATTN_ERR_HIP.
+ *   doc_stride, softcap <= 0 with ATTN_MOD_SOFTCAP), ATTN_ERR_UNSUPPORTED
+ *   (N >= 2^30), ATTN_ERR_WORKSPACE (bytes too small), ATTN_ERR_HIP.
  */
 size_t attn_mask_bytes(const attn_mask_spec *spec, int B, int N);
 attn_status attn_mask_build(const attn_mask_spec *spec, int B, int N, void *out,
@@ -127,8 +127,8 @@ attn_status attn_mask_build(const attn_mask_spec *spec, int B, int N, void *out,
  *     N, or NULL.  If NULL the call builds one in `workspace` first, which
  *     then needs attn_fwd_workspace_size bytes; otherwise workspace may be
  *     NULL with ws_bytes 0.
- * Supported: d in {64, 128}; Hq % Hkv == 0; N >= 0; B >= 0 (B*N == 0 is a
- * no-op).  Errors: ATTN_ERR_INVALID, ATTN_ERR_UNSUPPORTED (other d),
+ * Supported: d in {64, 128}; Hq % Hkv == 0; 0 <= N < 2^30; B >= 0 (B*N == 0
+ * is a no-op).  Errors: ATTN_ERR_INVALID, ATTN_ERR_UNSUPPORTED (other d),
  * ATTN_ERR_WORKSPACE, ATTN_ERR_HIP.
  */
 size_t attn_fwd_workspace_size(const attn_mask_spec *spec, int B, int N);
@@ -160,7 +160,8 @@ attn_status attn_fwd(attn_tensor q, attn_tensor k, attn_tensor v, attn_tensor o,
  *     that key.  For Lq = Lk this is the usual square mask.
  *   workspace: >= attn_fwd_varlen_workspace_size(total_q, total_k) bytes,
  *     16-byte aligned (the block mask is built there).
- * Supported: d in {64, 128}; Hq % Hkv == 0.  total_q == 0 is a no-op.
+ * Supported: d in {64, 128}; Hq % Hkv == 0; total_q, total_k < 2^30.
+ * total_q == 0 is a no-op.
  * Errors: ATTN_ERR_INVALID, ATTN_ERR_UNSUPPORTED, ATTN_ERR_WORKSPACE,
  * ATTN_ERR_HIP.
  */
@@ -215,7 +216,7 @@ attn_status attn_decode(attn_tensor q, attn_tensor k_cache, attn_tensor v_cache,
  *   workspace: >= attn_bwd_workspace_size(spec, B, Hq, N) bytes, 16-byte
  *     aligned (the call builds its block masks and per-row data there).
  *   q, k, v, o and dout token strides must be below 2^24 elements.
- * Supported: d in {64, 128}; Hq % Hkv == 0; not ATTN_MOD_ALIBI
+ * Supported: d in {64, 128}; Hq % Hkv == 0; N < 2^30; not ATTN_MOD_ALIBI
  * (ATTN_ERR_UNSUPPORTED).  Errors: ATTN_ERR_INVALID, ATTN_ERR_UNSUPPORTED,
  * ATTN_ERR_WORKSPACE, ATTN_ERR_HIP.
  */
@@ -257,7 +258,7 @@ attn_status attn_bwd(attn_tensor q, attn_tensor k, attn_tensor v, attn_tensor o,
  *   per_head set (its first block's scale is used for the whole head).
  *   o, lse, spec (not ATTN_MOD_ALIBI), scale, block_mask, workspace: as for
  *   attn_fwd.
- * Errors: ATTN_ERR_INVALID, ATTN_ERR_UNSUPPORTED (d != 128, ALiBi),
+ * Errors: ATTN_ERR_INVALID, ATTN_ERR_UNSUPPORTED (d != 128, N >= 2^30, ALiBi),
  * ATTN_ERR_WORKSPACE, ATTN_ERR_HIP.
  */
 size_t attn_quantize_fp8_workspace_size(int B, int H, int N);

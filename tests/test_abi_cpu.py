@@ -88,6 +88,7 @@ def test_fwd_validation_before_launch(lib):
     assert _fwd(lib, ws=ctypes.c_void_p(16), ws_bytes=8) == b.ATTN_ERR_WORKSPACE
     assert _fwd(lib, B=0) == b.ATTN_OK                               # empty: nothing to do
     assert _fwd(lib, N=0) == b.ATTN_OK
+    assert _fwd(lib, N=1 << 30) == b.ATTN_ERR_UNSUPPORTED            # longest sequence is 2^30 - 1
 
 
 def test_fwd_rejects_bad_specs(lib):
@@ -173,6 +174,8 @@ def test_varlen_validation_before_launch(lib):
     assert call(nseq=-1) == b.ATTN_ERR_INVALID
     assert call(nseq=0) == b.ATTN_ERR_INVALID            # rows but no sequence
     assert call(cu_q=None) == b.ATTN_ERR_INVALID
+    assert call(tq=1 << 30) == b.ATTN_ERR_UNSUPPORTED
+    assert call(tk=1 << 30) == b.ATTN_ERR_UNSUPPORTED
     assert call(flags=b.ATTN_MASK_DOCS) == b.ATTN_ERR_INVALID
     assert call() == b.ATTN_ERR_WORKSPACE
     assert call(tq=0) == b.ATTN_OK                         # nothing to do
