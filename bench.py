@@ -76,7 +76,7 @@ MEASURED_TRAFFIC = {
         "profiles/k_attn_fwd_d128_causal_b8_h32_n4096_d128.md"),
     "k_decode_split": (
         ["decode.hip", "common.h"],
-        "9919d73922911c4971de7ed8345be52bee59d62612c5cb7cd17e6ee4b611eb53",
+        "601096b821c62888892603a7db439cdb7b854af9fa54e412fa2477cb2cb75a96",
         958325877,
         "profiles/k_decode_split_decode_b16_gqa32x8_t32768_d128.md"),
     # all kernels of one attn_bwd call (mask_kv, prep, dQ, dK/dV)

@@ -87,8 +87,12 @@ __device__ __forceinline__ bool decode_item(const DecodeParams &p, int &b, int &
 
 // G: query heads per KV head, rounded up to a supported size (<= 16).
 // Scores live in LDS per wave, key-major: sc[key * GP + q], GP = max(G, 4).
+// Up to G = 8 a workgroup has up to 8 waves (two per SIMD, 256 registers
+// each); at G = 16 the 16 x 8 fp32 accumulators per lane need more, so
+// the workgroup has at most 4 waves and each wave the whole register file.
+template <int G> constexpr int decode_max_waves() { return G > 8 ? 4 : 8; }
 template <int D, int G>
-__global__ __launch_bounds__(512) void k_decode_split(DecodeParams p, int group) {
+__global__ __launch_bounds__(64 * decode_max_waves<G>()) void k_decode_split(DecodeParams p, int group) {
     constexpr int GP = G < 4 ? 4 : G;
     constexpr int KS = D / 32;   // k-steps of the 16x16x32 score MFMA
     constexpr int CH = D / 8;    // 16-byte chunks per row
@@ -364,19 +368,20 @@ __global__ __launch_bounds__(D) void k_decode_combine(DecodeParams p) {
 }
 
 // Waves per split workgroup: about one per DECODE_WAVE_KEYS keys of the
-// chunk, a power of two in [1, 8] that leaves a multiple of 64 keys per wave
-// (chunk is a multiple of 64; the V loop pads a slice to 32 or 64 keys).
+// chunk, a power of two in [1, max_waves] that leaves a multiple of 64 keys
+// per wave (chunk is a multiple of 64; the V loop pads a slice to 32 or 64
+// keys).
 constexpr int DECODE_WAVE_KEYS = 128;
-static int decode_waves(int chunk) {
+static int decode_waves(int chunk, int max_waves) {
     int n = 1;
-    while (n < 8 && 2 * n * DECODE_WAVE_KEYS <= chunk) n *= 2;
+    while (n < max_waves && 2 * n * DECODE_WAVE_KEYS <= chunk) n *= 2;
     while ((chunk / 64) % n) n /= 2;
     return n;
 }
 
 template <int D, int G> static hipError_t launch_split(const DecodeParams &p, int group, hipStream_t stream) {
     constexpr int GP = G < 4 ? 4 : G;
-    const int nwaves = decode_waves(p.chunk);
+    const int nwaves = decode_waves(p.chunk, decode_max_waves<G>());
     const size_t lds_scores = size_t(p.chunk) * GP * sizeof(float);
     const size_t lds_merge = (size_t(nwaves) * G * D + 2 * size_t(nwaves) * G) * sizeof(float);
     const size_t lds = lds_scores > lds_merge ? lds_scores : lds_merge;
