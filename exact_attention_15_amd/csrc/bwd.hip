@@ -262,7 +262,9 @@ template <int D> __device__ __forceinline__ void dma_offsets(int64_t sn, int wav
 // dQ.  One workgroup per (128-row query tile, query head, b), work mapped as
 // in the forward (groups sharing K/V on one XCD, heavy-first query tiles).
 // ---------------------------------------------------------------------------
-template <int D, bool SOFTCAP>
+// SAME_SN: K and V have the same token stride, so their tile DMAs share
+// one set of per-lane offsets (four fewer VGPRs held through the loop).
+template <int D, bool SOFTCAP, bool SAME_SN>
 __device__ __forceinline__ void bwd_dq_body(const BwdParams &p) {
     using C = FwdCfg<D>;
     lds_u8 *smem = (lds_u8 *)(smem_raw);
@@ -307,13 +309,14 @@ __device__ __forceinline__ void bwd_dq_body(const BwdParams &p) {
     const int32_t *tiles = p.mask.list + int64_t(item) * p.nkt;
     const uint16_t *kbase = p.k + b * p.k_sb + hk * p.k_sh;
     const uint16_t *vbase = p.v + b * p.v_sb + hk * p.v_sh;
-    uint32_t koff[C::LOADS], voff[C::LOADS];
+    uint32_t koff[C::LOADS], voff[SAME_SN ? 1 : C::LOADS];
     dma_offsets<D>(p.k_sn, wave, lane, koff);
-    dma_offsets<D>(p.v_sn, wave, lane, voff);
+    if constexpr (!SAME_SN) dma_offsets<D>(p.v_sn, wave, lane, voff);
+    const uint32_t *voffs = SAME_SN ? koff : voff;
     auto issue_tile = [&](int kt, int stage) {
         lds_u8 *kdst = smem + stage * C::STAGE_BYTES;
         dma_tile<D>(kbase, p.k_sn, kt * BLOCK_N, p.N, koff, kdst, wave, lane);
-        dma_tile<D>(vbase, p.v_sn, kt * BLOCK_N, p.N, voff, kdst + C::TILE_BYTES, wave, lane);
+        dma_tile<D>(vbase, p.v_sn, kt * BLOCK_N, p.N, voffs, kdst + C::TILE_BYTES, wave, lane);
     };
     BwdTile<D> tl;
     tl.init(col, half, lane);
@@ -570,11 +573,18 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdParams &p) {
 
 // Register budgets: the dQ kernel keeps Q and dO fragments and a d x 32
 // accumulator per wave; two waves per SIMD fit except with the soft cap at
-// d = 128 (at d = 128 without the cap a few registers spill, which costs
-// less than losing the second wave).  The dK/dV kernel keeps K and V
-// fragments and two accumulators: one wave per SIMD, accumulators in AGPRs.
+// d = 128.  At d = 128 without the cap, separate K and V DMA offsets leave
+// a few registers to spill, and each reload waits (vmcnt) on the tile DMAs
+// already in flight; with equal K and V token strides the offsets are
+// shared and nothing spills.  The dK/dV kernel keeps K and V fragments and
+// two accumulators: one wave per SIMD, accumulators in AGPRs.
 #define EXATTN_BWD_KERNELS(SUFFIX, D, SOFTCAP, DQ_WAVES)                                                     \
-    __global__ __launch_bounds__(256, DQ_WAVES) void k_bwd_dq_##SUFFIX(BwdParams p) { bwd_dq_body<D, SOFTCAP>(p); } \
+    __global__ __launch_bounds__(256, DQ_WAVES) void k_bwd_dq_##SUFFIX(BwdParams p) {                        \
+        bwd_dq_body<D, SOFTCAP, false>(p);                                                                   \
+    }                                                                                                          \
+    __global__ __launch_bounds__(256, DQ_WAVES) void k_bwd_dq_same_##SUFFIX(BwdParams p) {                   \
+        bwd_dq_body<D, SOFTCAP, true>(p);                                                                    \
+    }                                                                                                          \
     __global__ __launch_bounds__(256, 1) void k_bwd_dkdv_##SUFFIX(BwdParams p) { bwd_dkdv_body<D, SOFTCAP>(p); }
 EXATTN_BWD_KERNELS(d128, 128, false, 2)
 EXATTN_BWD_KERNELS(d128_softcap, 128, true, 1)
@@ -600,11 +610,14 @@ static hipError_t launch_bwd_d(const BwdParams &p, bool softcap, hipStream_t str
     if (e != hipSuccess) return e;
     void (*dq)(BwdParams);
     void (*dkdv)(BwdParams);
+    const bool same = p.k_sn == p.v_sn; // K and V DMAs can share their offsets
     if constexpr (D == 128) {
-        dq = softcap ? k_bwd_dq_d128_softcap : k_bwd_dq_d128;
+        dq = softcap ? (same ? k_bwd_dq_same_d128_softcap : k_bwd_dq_d128_softcap)
+                     : (same ? k_bwd_dq_same_d128 : k_bwd_dq_d128);
         dkdv = softcap ? k_bwd_dkdv_d128_softcap : k_bwd_dkdv_d128;
     } else {
-        dq = softcap ? k_bwd_dq_d64_softcap : k_bwd_dq_d64;
+        dq = softcap ? (same ? k_bwd_dq_same_d64_softcap : k_bwd_dq_d64_softcap)
+                     : (same ? k_bwd_dq_same_d64 : k_bwd_dq_d64);
         dkdv = softcap ? k_bwd_dkdv_d64_softcap : k_bwd_dkdv_d64;
     }
     e = launch_with_lds(dq, int64_t(p.B) * p.nqt * p.Hq, C::LDS_BYTES, p, stream);
