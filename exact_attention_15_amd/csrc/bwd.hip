@@ -441,11 +441,10 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdParams &p) {
     uint32_t qoff[C::LOADS], goff[C::LOADS];
     dma_offsets<D>(p.q_sn, wave, lane, qoff);
     dma_offsets<D>(p.do_sn, wave, lane, goff);
-    // tile index -> (query head, list entry)
-    auto entry = [&](int it) { return __builtin_amdgcn_readfirstlane(qlist[it % cnt]); };
+    // tile it -> query head hk * G + it / cnt and list entry it % cnt
     auto head = [&](int it) { return hk * G + it / cnt; };
-    auto issue_tile = [&](int it, int stage) {
-        const int h = head(it), qt = entry(it) >> 1, row0 = qt * BLOCK_N;
+    auto issue_tile = [&](int it, int ent, int stage) {
+        const int h = head(it), qt = ent >> 1, row0 = qt * BLOCK_N;
         lds_u8 *dst = smem + stage * STAGE;
         dma_tile<D>(p.q + b * p.q_sb + h * p.q_sh, p.q_sn, row0, p.N, qoff, dst, wave, lane);
         dma_tile<D>(p.dout + b * p.do_sb + h * p.do_sh, p.do_sn, row0, p.N, goff, dst + C::TILE_BYTES, wave, lane);
@@ -471,11 +470,18 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdParams &p) {
         adv[i] = f32x16_t{};
     }
 
+    // List entries are read one step before they are needed: the entry of
+    // tile it+1 was loaded during step it-1 and has arrived by that step's
+    // end-of-step wait, so no entry read is ever waited on alone (with one
+    // wave per SIMD nothing else would hide that latency).
+    int ent_cur = 0, ent_next_v = 0;
     auto step = [&](int it, const int stage) {
-        const int ent = entry(it);
+        const int ent = ent_cur;
         const int row0 = (ent >> 1) * BLOCK_N;
         const bool partial = ent & TILE_PARTIAL;
-        if (it + 1 < ntiles) issue_tile(it + 1, 1 - stage);
+        const int ent_next = __builtin_amdgcn_readfirstlane(ent_next_v);
+        const int ent_next2_v = qlist[min(it + 2, ntiles - 1) % cnt];
+        if (it + 1 < ntiles) issue_tile(it + 1, ent_next, 1 - stage);
         const lds_u8 *qs = smem + stage * STAGE;
         const lds_u8 *gs = qs + C::TILE_BYTES;
         const lds_u8 *rowd = gs + C::TILE_BYTES;
@@ -556,9 +562,15 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdParams &p) {
 
         wait_vmem_all();
         __syncthreads();
+        ent_cur = ent_next;
+        ent_next_v = ent_next2_v;
     };
 
-    if (ntiles > 0) issue_tile(0, 0);
+    if (ntiles > 0) {
+        ent_cur = __builtin_amdgcn_readfirstlane(qlist[0]);
+        issue_tile(0, ent_cur, 0);
+        ent_next_v = qlist[min(1, ntiles - 1) % cnt];
+    }
     wait_vmem_all();
     __syncthreads();
     for (int it = 0; it < ntiles; it += 2) {
