@@ -96,16 +96,25 @@ __device__ __forceinline__ void row_interval(const attn_mask_spec &spec, const V
 }
 
 // One workgroup (4 waves) per (query tile, b).  Threads 0..127 compute and
-// store the intervals of the tile's rows.  Then, 256 key tiles at a time,
-// wave w classifies key tiles w*64 + j (j = 0..63) one after another: every
-// lane tests two of the 128 rows and two ballots give "any row sees a key"
-// and "every row sees every key"; lane j keeps tile j's result.  The visited
-// tiles are then written in key order with a ballot/popcount compaction.
+// store the intervals of the tile's rows.  The key tiles are then classified
+// 256 at a time, thread t taking tile k0 + t:
+// - FULL (every row sees every key of the tile) holds exactly when the
+//   largest lo is at or before the tile's first key and the smallest hi at
+//   or after its last, both over the existing rows (a row with no visible
+//   key has lo > hi and so rules FULL out everywhere);
+// - visited (some row sees some key of it): row r touches the tiles
+//   lo_r/64 .. hi_r/64, so each row adds +1 and -1 at the two ends of that
+//   range in an LDS difference array, and a prefix sum gives every tile the
+//   number of rows that touch it.
+// The visited tiles are written in key order with a ballot/popcount
+// compaction.
 __global__ __launch_bounds__(256) void k_mask_tiles(attn_mask_spec spec, VarlenView vl, int N, int Nk, int nqt,
                                                     int nkt, int32_t *lo_out, int32_t *hi_out, int32_t *count_out,
                                                     int32_t *list_out) {
     __shared__ int32_t s_lo[BLOCK_M], s_hi[BLOCK_M];
-    __shared__ int32_t s_wcnt[4];
+    __shared__ int32_t s_diff[257];
+    __shared__ int32_t s_wsum[4];
+    __shared__ int32_t s_ext[2][4];
     const int qt = blockIdx.x, b = blockIdx.y, t = threadIdx.x;
     const int lane = t & 63, w = t >> 6;
     const int r0 = qt * BLOCK_M;
@@ -121,46 +130,73 @@ __global__ __launch_bounds__(256) void k_mask_tiles(attn_mask_spec spec, VarlenV
         s_hi[t] = hi;
     }
     __syncthreads();
-    // Rows past N are ignored; a row with no visible key (lo > hi) makes
-    // every tile PARTIAL but no tile visited.
-    const bool oka = r0 + lane < N, okb = r0 + lane + 64 < N;
-    const int lo_a = s_lo[lane], hi_a = s_hi[lane];
-    const int lo_b = s_lo[lane + 64], hi_b = s_hi[lane + 64];
+    // Largest lo and smallest hi over the existing rows (waves 0 and 1 hold
+    // rows 0..127; rows past N do not count).
+    if (w < 2) {
+        const bool ok = r0 + t < N;
+        int mlo = ok ? s_lo[t] : INT32_MIN, mhi = ok ? s_hi[t] : INT32_MAX;
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) {
+            mlo = max(mlo, __shfl_xor(mlo, o));
+            mhi = min(mhi, __shfl_xor(mhi, o));
+        }
+        if (lane == 0) {
+            s_ext[0][w] = mlo;
+            s_ext[1][w] = mhi;
+        }
+    }
+    __syncthreads();
+    const int max_lo = max(s_ext[0][0], s_ext[0][1]), min_hi = min(s_ext[1][0], s_ext[1][1]);
     const bool no_skip = spec.flags & ATTN_MASK_NO_SKIP;
     const int64_t item = int64_t(b) * nqt + qt;
     int32_t *list = list_out + item * nkt;
     int base = 0;
     for (int k0 = 0; k0 < nkt; k0 += 256) {
-        bool my_any = false, my_full = false;
-        const int kw = k0 + w * 64;
-        for (int j = 0; j < 64; ++j) {
-            const int kt = kw + j;
-            if (kt >= nkt) break; // wave-uniform
-            const int c0 = kt * BLOCK_N, c1 = c0 + BLOCK_N - 1;
-            const bool seen = (oka && max(lo_a, c0) <= min(hi_a, c1)) || (okb && max(lo_b, c0) <= min(hi_b, c1));
-            const bool gap = (oka && !(lo_a <= c0 && hi_a >= c1)) || (okb && !(lo_b <= c0 && hi_b >= c1));
-            bool any = __any(seen), full = !__any(gap);
-            if (no_skip) {
-                any = true;
-                full = false;
-            }
-            if (lane == j) {
-                my_any = any;
-                my_full = full;
+        s_diff[t] = 0;
+        if (t == 0) s_diff[256] = 0;
+        __syncthreads();
+        if (t < BLOCK_M && r0 + t < N) {
+            const int lo = s_lo[t], hi = s_hi[t];
+            if (lo <= hi) {
+                const int a = max(lo / BLOCK_N, k0), z = min(hi / BLOCK_N, k0 + 255);
+                if (a <= z) {
+                    atomicAdd(&s_diff[a - k0], 1);
+                    atomicAdd(&s_diff[z - k0 + 1], -1);
+                }
             }
         }
-        const uint64_t vis = __ballot(my_any);
-        if (lane == 0) s_wcnt[w] = __popcll(vis);
+        __syncthreads();
+        // inclusive prefix sum of s_diff[0..255]: wave scan, then wave totals
+        int v = s_diff[t];
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const int u = __shfl_up(v, o);
+            if (lane >= o) v += u;
+        }
+        if (lane == 63) s_wsum[w] = v;
+        __syncthreads();
+        for (int x = 0; x < w; ++x) v += s_wsum[x];
+        const int kt = k0 + t;
+        const int c0 = kt * BLOCK_N, c1 = c0 + BLOCK_N - 1;
+        bool any = kt < nkt && v > 0;
+        bool full = max_lo <= c0 && min_hi >= c1;
+        if (no_skip) {
+            any = kt < nkt;
+            full = false;
+        }
+        __syncthreads(); // s_wsum is reused for the compaction counts
+        const uint64_t vis = __ballot(any);
+        if (lane == 0) s_wsum[w] = __popcll(vis);
         __syncthreads();
         int woff = base;
-        for (int x = 0; x < w; ++x) woff += s_wcnt[x];
-        const int total = s_wcnt[0] + s_wcnt[1] + s_wcnt[2] + s_wcnt[3];
-        if (my_any) {
+        for (int x = 0; x < w; ++x) woff += s_wsum[x];
+        const int total = s_wsum[0] + s_wsum[1] + s_wsum[2] + s_wsum[3];
+        if (any) {
             const int pos = woff + __popcll(vis & ((uint64_t(1) << lane) - 1));
-            list[pos] = ((kw + lane) << 1) | (my_full ? 0 : TILE_PARTIAL);
+            list[pos] = (kt << 1) | (full ? 0 : TILE_PARTIAL);
         }
         base += total;
-        __syncthreads(); // s_wcnt is rewritten by the next round
+        __syncthreads(); // s_diff and s_wsum are rewritten by the next round
     }
     if (t == 0) count_out[item] = base;
 }
@@ -168,19 +204,32 @@ __global__ __launch_bounds__(256) void k_mask_tiles(attn_mask_spec spec, VarlenV
 // One workgroup per batch row: order[b][rank] = query tile, ranked by
 // descending visited-tile count (ties keep tile order), so the forward
 // kernel can hand out the heaviest query tiles of each batch row first.
+// The row's counts are staged in LDS when they fit (ORDER_LDS_TILES), so the
+// rank loop reads LDS broadcasts instead of global memory.
+constexpr int ORDER_LDS_TILES = 16384;
 __global__ __launch_bounds__(1024) void k_mask_order(int nqt, const int32_t *count, int32_t *order) {
+    extern __shared__ int32_t s_cnt[];
     const int b = blockIdx.x;
     const int32_t *cb = count + int64_t(b) * nqt;
     int32_t *ob = order + int64_t(b) * nqt;
-    for (int i = threadIdx.x; i < nqt; i += blockDim.x) {
-        const int ci = cb[i];
-        int rank = 0;
-        for (int j = 0; j < nqt; ++j) {
-            const int cj = cb[j];
-            rank += (cj > ci) || (cj == ci && j < i);
-        }
-        ob[rank] = i;
+    const bool in_lds = nqt <= ORDER_LDS_TILES;
+    if (in_lds) {
+        for (int i = threadIdx.x; i < nqt; i += blockDim.x) s_cnt[i] = cb[i];
+        __syncthreads();
     }
+    auto rank_all = [&](const auto *c) {
+        for (int i = threadIdx.x; i < nqt; i += blockDim.x) {
+            const int ci = c[i];
+            int rank = 0;
+            for (int j = 0; j < nqt; ++j) {
+                const int cj = c[j];
+                rank += (cj > ci) || (cj == ci && j < i);
+            }
+            ob[rank] = i;
+        }
+    };
+    if (in_lds) rank_all((const __attribute__((address_space(3))) int32_t *)(s_cnt)); // generic -> LDS
+    else rank_all(cb);
 }
 
 hipError_t launch_mask_build(const attn_mask_spec &spec, const MaskLayout &L, void *out,
@@ -195,7 +244,8 @@ hipError_t launch_mask_build(const attn_mask_spec &spec, const MaskLayout &L, vo
                        lo, hi, cnt, list);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k_mask_order, dim3(L.B), dim3(1024), 0, stream, L.nqt, cnt, order);
+    const size_t order_lds = L.nqt <= ORDER_LDS_TILES ? size_t(L.nqt) * sizeof(int32_t) : 0;
+    hipLaunchKernelGGL(k_mask_order, dim3(L.B), dim3(1024), order_lds, stream, L.nqt, cnt, order);
     return hipGetLastError();
 }
 
