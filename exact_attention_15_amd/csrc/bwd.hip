@@ -38,8 +38,9 @@ extern __shared__ __attribute__((aligned(1024))) uint8_t smem_raw[];
 // holding a visible (row, key) pair, ascending, each FULL or PARTIAL.  A tile
 // is FULL when all its 64 rows exist and see every key of the block that
 // exists.  Wave w classifies query tiles w*64 + j (j = 0..63) of each round
-// of 256, one after another with lane = row and two ballots; the visited
-// tiles are compacted in order with a ballot/popcount prefix.
+// of 256, one after another with lane = row and two ballots (the rows'
+// intervals loaded eight tiles at a time); the visited tiles are compacted
+// in order with a ballot/popcount prefix.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_bwd_mask_kv(int N, int nkb, int nqt64, uint32_t flags,
                                                      const int32_t *lo_in, const int32_t *hi_in,
@@ -55,26 +56,37 @@ __global__ __launch_bounds__(256) void k_bwd_mask_kv(int N, int nkb, int nqt64, 
     for (int k0 = 0; k0 < nqt64; k0 += 256) {
         bool my_any = false, my_full = false;
         const int kw = k0 + w * 64;
-        for (int j = 0; j < 64; ++j) {
-            const int qt = kw + j;
-            if (qt >= nqt64) break; // wave-uniform
-            const int row = qt * BLOCK_N + lane;
-            const bool ok = row < N;
-            int lo = 1, hi = 0;
-            if (ok) {
-                lo = lo_in[int64_t(b) * N + row];
-                hi = hi_in[int64_t(b) * N + row];
+        // eight query tiles per batch: their row intervals are all requested
+        // before the first is used, one memory round trip per batch
+        for (int j0 = 0; j0 < 64; j0 += 8) {
+            if (kw + j0 >= nqt64) break; // wave-uniform
+            int lo[8], hi[8];
+            bool ok[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int row = (kw + j0 + u) * BLOCK_N + lane;
+                ok[u] = kw + j0 + u < nqt64 && row < N;
+                lo[u] = 1;
+                hi[u] = 0;
+                if (ok[u]) {
+                    lo[u] = lo_in[int64_t(b) * N + row];
+                    hi[u] = hi_in[int64_t(b) * N + row];
+                }
             }
-            const bool seen = ok && max(lo, c0) <= min(hi, c1);
-            const bool gap = !ok || !(lo <= c0 && hi >= c1);
-            bool any = __any(seen), full = !__any(gap);
-            if (no_skip) {
-                any = true;
-                full = false;
-            }
-            if (lane == j) {
-                my_any = any;
-                my_full = full;
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                if (kw + j0 + u >= nqt64) break; // wave-uniform
+                const bool seen = ok[u] && max(lo[u], c0) <= min(hi[u], c1);
+                const bool gap = !ok[u] || !(lo[u] <= c0 && hi[u] >= c1);
+                bool any = __any(seen), full = !__any(gap);
+                if (no_skip) {
+                    any = true;
+                    full = false;
+                }
+                if (lane == j0 + u) {
+                    my_any = any;
+                    my_full = full;
+                }
             }
         }
         const uint64_t vis = __ballot(my_any);
