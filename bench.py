@@ -72,23 +72,23 @@ MEASURED_TRAFFIC = {
     "k_attn_fwd_d128": (
         ["fwd.hip", "tile.h", "common.h"],
         "432176192ba15b9ea9ef0fb2539addbef0684f4b8f0a17c9bab299bde3485917",
-        1118126762,
+        1117455680,
         "profiles/k_attn_fwd_d128_causal_b8_h32_n4096_d128.md"),
     "k_decode_split": (
         ["decode.hip", "common.h"],
         "601096b821c62888892603a7db439cdb7b854af9fa54e412fa2477cb2cb75a96",
-        958325877,
+        958346756,
         "profiles/k_decode_split_decode_b16_gqa32x8_t32768_d128.md"),
     # all kernels of one attn_bwd call (mask_kv, prep, dQ, dK/dV)
     "attn_bwd_d128": (
         ["bwd.hip", "tile.h", "common.h"],
-        "8a565bac454c0e417832d1e37bb7fc0f9977daa64385b568e30188ae282a6314",
-        3563426020,
+        "e692615f73b7981f18fa85791ec16f59b05183d4a554677530cce5ad79b59d87",
+        3601989294,
         "profiles/k_bwd_d128_causal_b8_h32_n4096_d128.md"),
     "k_attn_fwd8_d128": (
         ["fwd8.hip", "tile.h", "common.h"],
         "ef7c0aecb2781218a80f54367d05cae251ac116e2ca3712d5651f3951d738849",
-        679381880,
+        679386743,
         "profiles/k_attn_fwd8_d128_causal_b8_h32_n4096_d128.md"),
 }
 
