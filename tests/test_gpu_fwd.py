@@ -183,18 +183,24 @@ def _host_intervals(kind, B, N, docs):
     if kind == "window":
         lo = np.maximum(lo, i - 300)
         hi = np.minimum(hi, i + 300)
+    if kind == "ahead":  # window (-40, 100): keys i+40 .. i+100, the last 40 rows see none
+        lo = np.maximum(lo, i + 40)
+        hi = np.minimum(hi, i + 100)
     if kind == "docs":
         for b in range(B):
             offs = docs[b]
             idx = np.searchsorted(offs, i, side="right") - 1
             lo[b] = np.maximum(lo[b], offs[idx])
             hi[b] = np.minimum(hi[b], offs[idx + 1] - 1)
+    empty = lo > hi  # rows with no visible key are stored as lo = 1, hi = 0
+    lo[empty], hi[empty] = 1, 0
     return lo, hi
 
 
-@pytest.mark.parametrize("kind", ["causal", "window", "docs"])
-@pytest.mark.parametrize("N", [256, 1000, 4096])
+@pytest.mark.parametrize("kind", ["causal", "window", "docs", "ahead"])
+@pytest.mark.parametrize("N", [256, 1000, 4096, 20000])
 def test_mask_builder_matches_host(ea, kind, N):
+    # N = 20000 has 313 key tiles: the builder classifies them in two rounds
     B = 2
     docs_dev = None
     docs = None
@@ -202,8 +208,8 @@ def test_mask_builder_matches_host(ea, kind, N):
         rng = np.random.Generator(np.random.PCG64(N))
         docs = gen.draw_doc_offsets(rng, B, N, 64, 900)
         _, docs_dev = _docs_dev(docs, N)
-    spec = ea.MaskSpec(causal=kind in ("causal", "docs"), window=300 if kind == "window" else None,
-                       doc_offsets=docs_dev)
+    window = 300 if kind == "window" else ((-40, 100) if kind == "ahead" else None)
+    spec = ea.MaskSpec(causal=kind in ("causal", "docs"), window=window, doc_offsets=docs_dev)
     bm = ea.mask_build(spec, B, N)
     torch.cuda.synchronize()
     m = ea.mask_unpack(bm, B, N)
@@ -212,16 +218,15 @@ def test_mask_builder_matches_host(ea, kind, N):
     nqt, nkt = m["nqt"], m["nkt"]
     BM, BN = ea.BLOCK_M, ea.BLOCK_N
     counts = np.zeros((B, nqt), np.int64)
+    c0 = np.arange(nkt) * BN
+    c1 = c0 + BN - 1
     for b in range(B):
         for qt in range(nqt):
             rows = np.arange(qt * BM, min(N, qt * BM + BM))
-            expect = []
-            for kt in range(nkt):
-                c0, c1 = kt * BN, kt * BN + BN - 1
-                any_vis = np.any(np.maximum(lo[b, rows], c0) <= np.minimum(hi[b, rows], c1))
-                full = np.all((lo[b, rows] <= c0) & (hi[b, rows] >= c1))
-                if any_vis:
-                    expect.append(kt * 2 + (0 if full else 1))
+            lr, hr = lo[b, rows][:, None], hi[b, rows][:, None]
+            any_vis = np.any(np.maximum(lr, c0) <= np.minimum(hr, c1), axis=0)
+            full = np.all((lr <= c0) & (hr >= c1), axis=0)
+            expect = [kt * 2 + (0 if full[kt] else 1) for kt in range(nkt) if any_vis[kt]]
             counts[b, qt] = len(expect)
             got = m["list"][b, qt, : len(expect)].numpy().tolist()
             assert m["count"][b, qt].item() == len(expect)
@@ -233,6 +238,23 @@ def test_mask_builder_matches_host(ea, kind, N):
         assert sorted(order[b].tolist()) == list(range(nqt))
         expect_order = sorted(range(nqt), key=lambda x: (-counts[b, x], x))
         assert order[b].tolist() == expect_order
+
+
+@pytest.mark.parametrize("N", [1000, 20000])
+def test_mask_builder_no_skip(ea, N):
+    # ATTN_MASK_NO_SKIP lists every key tile of every query tile as PARTIAL
+    # (element masks everywhere), whatever the mask
+    B = 2
+    bm = ea.mask_build(ea.MaskSpec(causal=True, no_skip=True), B, N)
+    torch.cuda.synchronize()
+    m = ea.mask_unpack(bm, B, N)
+    nqt, nkt = m["nqt"], m["nkt"]
+    expect = [2 * kt + 1 for kt in range(nkt)]
+    assert np.all(m["count"].numpy() == nkt)
+    for b in range(B):
+        for qt in range(nqt):
+            assert m["list"][b, qt, :nkt].numpy().tolist() == expect, (b, qt)
+    assert np.array_equal(m["order"].numpy().reshape(B, nqt), np.tile(np.arange(nqt), (B, 1)))
 
 
 @pytest.mark.parametrize("d", [64, 128])
