@@ -13,8 +13,12 @@ LIB = os.path.join(HERE, "libexattn.so")
 SOURCES = ["abi.hip", "mask.hip", "fwd.hip", "fwd8.hip", "bwd.hip", "decode.hip", "quant.hip"]
 # The forward kernel relies on no NaN semantics (masked scores are -inf), so
 # it drops IEEE NaN quieting: max/min then need no canonicalising moves.
+# The backward kernels take every MFMA result in VGPRs: the score products
+# are read by the VALU, and left to its heuristic the compiler put them in
+# AGPRs and moved the dK/dV accumulators between the two register files
+# every tile (hundreds of v_accvgpr copies per tile).
 EXTRA = {"fwd.hip": ["-mno-amdgpu-ieee", "-fno-honor-nans"], "fwd8.hip": ["-mno-amdgpu-ieee", "-fno-honor-nans"],
-         "bwd.hip": ["-mno-amdgpu-ieee", "-fno-honor-nans"]}
+         "bwd.hip": ["-mno-amdgpu-ieee", "-fno-honor-nans", "-mllvm", "--amdgpu-mfma-vgpr-form=1"]}
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 FLAGS = [
