@@ -66,29 +66,30 @@ CSRC = os.path.join(ROOT, "exact_attention_15_amd", "csrc")
 # (--calibrate-copy): FETCH_SIZE counts half of the bytes a copy reads,
 # WRITE_SIZE all of those it writes.  A figure holds only for the kernel
 # source it was taken on; if the sources' sha256 differs it is reported as
-# null (stale).
+# null (stale).  The build script is hashed with the sources, since its
+# per-file compiler flags change the kernels' machine code too.
 MEASURED_TRAFFIC = {
     # kernel: (sources, sha256 of their concatenation, bytes per launch, summary)
     "k_attn_fwd_d128": (
-        ["fwd.hip", "tile.h", "common.h"],
-        "432176192ba15b9ea9ef0fb2539addbef0684f4b8f0a17c9bab299bde3485917",
-        1117455680,
+        ["fwd.hip", "tile.h", "common.h", "../build.py"],
+        "7c27c81005dd02fbb2328209dc0787ada9f819f8056620fb11d9e037971f5ca8",
+        1117774156,
         "profiles/k_attn_fwd_d128_causal_b8_h32_n4096_d128.md"),
     "k_decode_split": (
-        ["decode.hip", "common.h"],
-        "601096b821c62888892603a7db439cdb7b854af9fa54e412fa2477cb2cb75a96",
-        958346756,
+        ["decode.hip", "common.h", "../build.py"],
+        "7bc7b42e2a5aa0123624f451187d7a4764dc0e1f245be004cdae91e6fc497e9e",
+        958342936,
         "profiles/k_decode_split_decode_b16_gqa32x8_t32768_d128.md"),
     # all kernels of one attn_bwd call (mask_kv, prep, dQ, dK/dV)
     "attn_bwd_d128": (
-        ["bwd.hip", "tile.h", "common.h"],
-        "e692615f73b7981f18fa85791ec16f59b05183d4a554677530cce5ad79b59d87",
-        3601989294,
+        ["bwd.hip", "tile.h", "common.h", "../build.py"],
+        "00018f0537eb63034760bd7c5856967d813a624319b17e99c9cb9a8c49022ac1",
+        3602290789,
         "profiles/k_bwd_d128_causal_b8_h32_n4096_d128.md"),
     "k_attn_fwd8_d128": (
-        ["fwd8.hip", "tile.h", "common.h"],
-        "ef7c0aecb2781218a80f54367d05cae251ac116e2ca3712d5651f3951d738849",
-        679386743,
+        ["fwd8.hip", "tile.h", "common.h", "../build.py"],
+        "bfb09f8e45c098f3c84a9e6cbec5074081dbc9bbb8a9e31c1511caa4af200e05",
+        679390709,
         "profiles/k_attn_fwd8_d128_causal_b8_h32_n4096_d128.md"),
 }
 
