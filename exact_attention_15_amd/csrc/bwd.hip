@@ -106,30 +106,45 @@ __global__ __launch_bounds__(256) void k_bwd_mask_kv(int N, int nkb, int nqt64, 
 }
 
 // ---------------------------------------------------------------------------
-// Per row: D = dO . O (fp32) and the base-2 LSE.  16 lanes per row.
+// Per row: D = dO . O (fp32) and the base-2 LSE.  16 lanes per row; each
+// 16-lane group takes PREP_ROWS rows and issues all their loads before
+// using any.  Grid (row blocks, Hq, B): no index division.
 // ---------------------------------------------------------------------------
+constexpr int PREP_ROWS = 4;
+constexpr int PREP_BLOCK_ROWS = 16 * PREP_ROWS; // 256 threads = 16 groups of 16 lanes
 template <int D>
 __global__ __launch_bounds__(256) void k_bwd_prep(BwdParams p) {
-    constexpr int LPR = 16, PER = D / LPR; // lanes per row, elements per lane
-    const int64_t gid = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
-    const int64_t r = gid / LPR;
-    const int part = int(gid % LPR);
-    const int64_t rows = int64_t(p.B) * p.Hq * p.N;
-    float acc = 0.f;
-    if (r < rows) {
-        const int b = int(r / (int64_t(p.Hq) * p.N)), h = int((r / p.N) % p.Hq), i = int(r % p.N);
-        const uint16_t *o = p.o + b * p.o_sb + h * p.o_sh + int64_t(i) * p.o_sn + PER * part;
-        const uint16_t *g = p.dout + b * p.do_sb + h * p.do_sh + int64_t(i) * p.do_sn + PER * part;
+    constexpr int LPR = 16, PER = D / LPR; // lanes per row, elements per lane (8 or 4)
+    typedef uint32_t vec_t __attribute__((ext_vector_type(PER / 2)));
+    const int part = threadIdx.x % LPR, grp = threadIdx.x / LPR;
+    const int h = blockIdx.y, b = blockIdx.z;
+    const int i0 = blockIdx.x * PREP_BLOCK_ROWS + grp * PREP_ROWS;
+    vec_t ov[PREP_ROWS], gv[PREP_ROWS];
 #pragma unroll
-        for (int e = 0; e < PER; ++e)
-            acc += __builtin_bit_cast(float, uint32_t(o[e]) << 16) * __builtin_bit_cast(float, uint32_t(g[e]) << 16);
+    for (int k = 0; k < PREP_ROWS; ++k) {
+        const int i = min(i0 + k, p.N - 1); // rows past N re-read row N-1, result dropped
+        ov[k] = *reinterpret_cast<const vec_t *>(p.o + b * p.o_sb + h * p.o_sh + int64_t(i) * p.o_sn + PER * part);
+        gv[k] = *reinterpret_cast<const vec_t *>(p.dout + b * p.do_sb + h * p.do_sh + int64_t(i) * p.do_sn +
+                                                 PER * part);
     }
 #pragma unroll
-    for (int off = 1; off < LPR; off <<= 1) acc += __shfl_xor(acc, off);
-    if (r < rows && part == 0) {
-        p.dvec[r] = acc;
-        const float l = p.lse[r];
-        p.lse2[r] = l == -INFINITY ? INFINITY : l * LOG2E;
+    for (int k = 0; k < PREP_ROWS; ++k) {
+        float acc = 0.f;
+#pragma unroll
+        for (int e = 0; e < PER / 2; ++e) {
+            const uint32_t x = ov[k][e], y = gv[k][e];
+            acc += __builtin_bit_cast(float, x << 16) * __builtin_bit_cast(float, y << 16);
+            acc += __builtin_bit_cast(float, x & 0xffff0000u) * __builtin_bit_cast(float, y & 0xffff0000u);
+        }
+#pragma unroll
+        for (int off = 1; off < LPR; off <<= 1) acc += __shfl_xor(acc, off);
+        const int i = i0 + k;
+        if (i < p.N && part == 0) {
+            const int64_t r = (int64_t(b) * p.Hq + h) * p.N + i;
+            p.dvec[r] = acc;
+            const float l = p.lse[r];
+            p.lse2[r] = l == -INFINITY ? INFINITY : l * LOG2E;
+        }
     }
 }
 
@@ -628,8 +643,8 @@ static hipError_t launch_with_lds(void (*kernel)(BwdParams), int64_t nblocks, si
 template <int D>
 static hipError_t launch_bwd_d(const BwdParams &p, bool softcap, hipStream_t stream) {
     using C = FwdCfg<D>;
-    const int64_t rows = int64_t(p.B) * p.Hq * p.N;
-    hipLaunchKernelGGL((k_bwd_prep<D>), dim3(unsigned((rows * 16 + 255) / 256)), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((k_bwd_prep<D>), dim3(unsigned((p.N + PREP_BLOCK_ROWS - 1) / PREP_BLOCK_ROWS), p.Hq, p.B),
+                       dim3(256), 0, stream, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     void (*dq)(BwdParams);
