@@ -73,23 +73,23 @@ MEASURED_TRAFFIC = {
     "k_attn_fwd_d128": (
         ["fwd.hip", "tile.h", "common.h", "../build.py"],
         "7c27c81005dd02fbb2328209dc0787ada9f819f8056620fb11d9e037971f5ca8",
-        1117774156,
+        1118222921,
         "profiles/k_attn_fwd_d128_causal_b8_h32_n4096_d128.md"),
     "k_decode_split": (
         ["decode.hip", "common.h", "../build.py"],
         "7bc7b42e2a5aa0123624f451187d7a4764dc0e1f245be004cdae91e6fc497e9e",
-        958342936,
+        958343927,
         "profiles/k_decode_split_decode_b16_gqa32x8_t32768_d128.md"),
     # all kernels of one attn_bwd call (mask_kv, prep, dQ, dK/dV)
     "attn_bwd_d128": (
         ["bwd.hip", "tile.h", "common.h", "../build.py"],
-        "00018f0537eb63034760bd7c5856967d813a624319b17e99c9cb9a8c49022ac1",
-        3602290789,
+        "5e9a5362a2438cd9eda905d30a73d21bb5017cf46e3f8e5ae6ed5714cc8947e1",
+        3603356191,
         "profiles/k_bwd_d128_causal_b8_h32_n4096_d128.md"),
     "k_attn_fwd8_d128": (
         ["fwd8.hip", "tile.h", "common.h", "../build.py"],
         "bfb09f8e45c098f3c84a9e6cbec5074081dbc9bbb8a9e31c1511caa4af200e05",
-        679390709,
+        679384764,
         "profiles/k_attn_fwd8_d128_causal_b8_h32_n4096_d128.md"),
 }
 
