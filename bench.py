@@ -77,7 +77,7 @@ MEASURED_TRAFFIC = {
         "profiles/k_attn_fwd_d128_causal_b8_h32_n4096_d128.md"),
     "k_decode_split": (
         ["decode.hip", "common.h", "../build.py"],
-        "7bc7b42e2a5aa0123624f451187d7a4764dc0e1f245be004cdae91e6fc497e9e",
+        "7910928147fecd0f6b97f37b6102d5f5a04cecb2afd912e8a46d7ce2318c62f0",
         958343927,
         "profiles/k_decode_split_decode_b16_gqa32x8_t32768_d128.md"),
     # all kernels of one attn_bwd call (mask_kv, prep, dQ, dK/dV)

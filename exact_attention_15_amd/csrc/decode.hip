@@ -87,10 +87,13 @@ __device__ __forceinline__ bool decode_item(const DecodeParams &p, int &b, int &
 
 // G: query heads per KV head, rounded up to a supported size (<= 16).
 // Scores live in LDS per wave, key-major: sc[key * GP + q], GP = max(G, 4).
-// Up to G = 8 a workgroup has up to 8 waves (two per SIMD, 256 registers
-// each); at G = 16 the 16 x 8 fp32 accumulators per lane need more, so
-// the workgroup has at most 4 waves and each wave the whole register file.
-template <int G> constexpr int decode_max_waves() { return G > 8 ? 4 : 8; }
+// Up to G = 4 a workgroup has up to 8 waves (two per SIMD).  From G = 8
+// the G x 8 fp32 accumulators per lane raise the register count (G = 8: 155
+// VGPRs, three waves per SIMD; G = 16: the whole register file), and a
+// workgroup has at most 4 waves, one per SIMD, so that as many workgroups as
+// the registers allow share a CU (an 8-wave workgroup at G = 8 left one CU
+// with a single workgroup).
+template <int G> constexpr int decode_max_waves() { return G > 4 ? 4 : 8; }
 template <int D, int G>
 __global__ __launch_bounds__(64 * decode_max_waves<G>()) void k_decode_split(DecodeParams p, int group) {
     constexpr int GP = G < 4 ? 4 : G;
