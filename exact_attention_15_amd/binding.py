@@ -121,6 +121,47 @@ def _check_bf16(name, t):
         raise ValueError(f"{name}: the head dimension must be contiguous")
 
 
+def _check_out(name, t, shape, dtype, device, contiguous=False):
+    """A caller-supplied output buffer must match what the call writes: the
+    C ABI takes only pointers and strides, so a smaller or mistyped buffer
+    would be written out of bounds."""
+    if not isinstance(t, torch.Tensor) or t.dtype != dtype or t.device != device:
+        raise TypeError(f"{name}: expected a {dtype} tensor on {device}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: expected shape {tuple(shape)}, got {tuple(t.shape)}")
+    if contiguous and not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+    if dtype == torch.bfloat16 and t.numel() and t.stride(-1) != 1:
+        raise ValueError(f"{name}: the head dimension must be contiguous")
+
+
+def _check_block_mask(lib, block_mask, spec, B, N, device):
+    """A prebuilt block mask must be a uint8 device buffer at least as large
+    as the layout for (B, N) (attn_mask_bytes)."""
+    if (not isinstance(block_mask, torch.Tensor) or block_mask.dtype != torch.uint8
+            or block_mask.device != device or not block_mask.is_contiguous()):
+        raise TypeError(f"block_mask: expected a contiguous uint8 tensor on {device} (from mask_build)")
+    need = lib.attn_mask_bytes(spec.ref(), B, N)
+    if block_mask.numel() < need:
+        raise ValueError(f"block_mask: {block_mask.numel()} bytes, the mask for B={B}, N={N} "
+                         f"needs {need}")
+
+
+def _check_spec(spec, B, Hq, device):
+    """The spec's device arrays are read per batch row (document offsets) and
+    per query head (ALiBi slopes)."""
+    if spec.doc_offsets is not None:
+        if spec.doc_offsets.device != device:
+            raise TypeError(f"doc_offsets: expected a tensor on {device}")
+        if spec.doc_offsets.shape[0] < B:
+            raise ValueError(f"doc_offsets: {spec.doc_offsets.shape[0]} rows for B={B} batch rows")
+    if spec.alibi_slopes is not None:
+        if spec.alibi_slopes.device != device:
+            raise TypeError(f"alibi_slopes: expected a tensor on {device}")
+        if Hq is not None and spec.alibi_slopes.numel() != Hq:
+            raise ValueError("alibi_slopes must hold one slope per query head")
+
+
 def _stream(device) -> ctypes.c_void_p:
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
@@ -169,6 +210,7 @@ def mask_build(spec: MaskSpec, B: int, N: int, device=None) -> torch.Tensor:
     """Build a reusable block mask (a uint8 device buffer)."""
     lib = _load()
     device = device or torch.device("cuda", torch.cuda.current_device())
+    _check_spec(spec, B, None, device)
     nbytes = lib.attn_mask_bytes(spec.ref(), B, N)
     buf = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
     _check(lib.attn_mask_build(spec.ref(), B, N, buf.data_ptr(), nbytes, _stream(device)))
@@ -190,19 +232,22 @@ def fwd(q, k, v, *, causal=False, window=None, doc_offsets=None, softcap=None,
     if spec is None:
         spec = MaskSpec(causal=causal, window=window, doc_offsets=doc_offsets,
                         softcap=softcap, no_skip=no_skip, alibi_slopes=alibi_slopes)
-    if spec.alibi_slopes is not None and spec.alibi_slopes.numel() != Hq:
-        raise ValueError("alibi_slopes must hold one slope per query head")
+    _check_spec(spec, B, Hq, q.device)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     if out is None:
         out = torch.empty((B, Hq, N, d), dtype=torch.bfloat16, device=q.device)
+    _check_out("out", out, (B, Hq, N, d), torch.bfloat16, q.device)
     if lse is None:
         lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device)
+    _check_out("lse", lse, (B, Hq, N), torch.float32, q.device, contiguous=True)
     ws = None
     ws_bytes = 0
     if block_mask is None:
         ws_bytes = lib.attn_fwd_workspace_size(spec.ref(), B, N)
         ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=q.device)
+    else:
+        _check_block_mask(lib, block_mask, spec, B, N, q.device)
     st = lib.attn_fwd(_tensor4(q), _tensor4(k), _tensor4(v), _tensor4(out), lse.data_ptr(),
                       B, Hq, Hkv, N, d, spec.ref(), float(scale),
                       None if block_mask is None else block_mask.data_ptr(),
@@ -240,9 +285,13 @@ def fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, *, causal=False, window=None
         scale = 1.0 / math.sqrt(d)
     if out is None:
         out = torch.empty((tq, Hq, d), dtype=torch.bfloat16, device=q.device)
+    _check_out("out", out, (tq, Hq, d), torch.bfloat16, q.device)
     if lse is None:
         lse = torch.empty((Hq, tq), dtype=torch.float32, device=q.device)
+    _check_out("lse", lse, (Hq, tq), torch.float32, q.device, contiguous=True)
     ws_bytes = lib.attn_fwd_varlen_workspace_size(tq, tk)
+    if workspace is not None and (workspace.dtype != torch.uint8 or workspace.device != q.device):
+        raise TypeError(f"workspace: expected a uint8 tensor on {q.device}")
     if workspace is None or workspace.numel() < ws_bytes:
         workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=q.device)
     st = lib.attn_fwd_varlen(_tensor3(q), _tensor3(k), _tensor3(v), _tensor3(out), lse.data_ptr(),
@@ -277,6 +326,7 @@ def bwd(q, k, v, o, lse, dout, *, causal=False, window=None, doc_offsets=None,
     if spec is None:
         spec = MaskSpec(causal=causal, window=window, doc_offsets=doc_offsets,
                         softcap=softcap, no_skip=no_skip)
+    _check_spec(spec, B, Hq, q.device)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     if dq is None:
@@ -285,9 +335,13 @@ def bwd(q, k, v, o, lse, dout, *, causal=False, window=None, doc_offsets=None,
         dk = torch.empty((B, Hkv, N, d), dtype=torch.bfloat16, device=q.device)
     if dv is None:
         dv = torch.empty((B, Hkv, N, d), dtype=torch.bfloat16, device=q.device)
-    for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
-        _check_bf16(name, t)
+    if lse.device != q.device:
+        raise TypeError(f"lse: expected a tensor on {q.device}")
+    for name, t, shape in (("dq", dq, (B, Hq, N, d)), ("dk", dk, (B, Hkv, N, d)), ("dv", dv, (B, Hkv, N, d))):
+        _check_out(name, t, shape, torch.bfloat16, q.device)
     ws_bytes = lib.attn_bwd_workspace_size(spec.ref(), B, Hq, N)
+    if workspace is not None and (workspace.dtype != torch.uint8 or workspace.device != q.device):
+        raise TypeError(f"workspace: expected a uint8 tensor on {q.device}")
     if workspace is None or workspace.numel() < ws_bytes:
         workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=q.device)
     st = lib.attn_bwd(_tensor4(q), _tensor4(k), _tensor4(v), _tensor4(o), lse.data_ptr(),
@@ -357,20 +411,25 @@ def fwd_fp8(q8, k8, v8, q_scales, k_scales, v_scales, *, causal=False, window=No
     if spec is None:
         spec = MaskSpec(causal=causal, window=window, doc_offsets=doc_offsets, softcap=softcap,
                         no_skip=no_skip)
+    _check_spec(spec, B, Hq, q8.device)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     if out is None:
         out = torch.empty((B, Hq, N, d), dtype=torch.bfloat16, device=q8.device)
+    _check_out("out", out, (B, Hq, N, d), torch.bfloat16, q8.device)
     if lse is None:
         lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q8.device)
+    _check_out("lse", lse, (B, Hq, N), torch.float32, q8.device, contiguous=True)
     for name, t in (("q_scales", q_scales), ("k_scales", k_scales), ("v_scales", v_scales)):
-        if t.dtype != torch.float32 or not t.is_cuda or not t.is_contiguous():
-            raise TypeError(f"{name}: expected a contiguous fp32 GPU tensor")
+        if t.dtype != torch.float32 or t.device != q8.device or not t.is_contiguous():
+            raise TypeError(f"{name}: expected a contiguous fp32 tensor on {q8.device}")
     ws = None
     ws_bytes = 0
     if block_mask is None:
         ws_bytes = lib.attn_fwd_workspace_size(spec.ref(), B, N)
         ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=q8.device)
+    else:
+        _check_block_mask(lib, block_mask, spec, B, N, q8.device)
     st = lib.attn_fwd_fp8(_tensor4u8(q8), _tensor4u8(k8), _tensor4u8(v8), q_scales.data_ptr(),
                           k_scales.data_ptr(), v_scales.data_ptr(), _tensor4(out), lse.data_ptr(),
                           B, Hq, Hkv, N, d, spec.ref(), float(scale),
@@ -387,19 +446,33 @@ def decode(q, k_cache, v_cache, lens, *, scale=None, chunk=1024, out=None, lse=N
     lib = _load()
     for name, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache)):
         _check_bf16(name, t)
+    if q.dim() not in (3, 4) or (q.dim() == 4 and q.shape[2] != 1):
+        raise ValueError(f"q: expected [B, Hq, d] or [B, Hq, 1, d], got {tuple(q.shape)}")
     q4 = q if q.dim() == 4 else q.unsqueeze(2)
     B, Hq, _, d = q4.shape
+    if k_cache.dim() != 4:
+        raise ValueError(f"k_cache: expected [B, Hkv, T, d], got {tuple(k_cache.shape)}")
     Hkv, T = k_cache.shape[1], k_cache.shape[2]
-    if lens.dtype != torch.int32 or not lens.is_cuda or lens.numel() != B:
-        raise TypeError("lens: expected int32 [B] on the GPU")
+    if tuple(k_cache.shape) != (B, Hkv, T, d) or tuple(v_cache.shape) != (B, Hkv, T, d):
+        raise ValueError(f"k_cache and v_cache must both be [B, Hkv, T, d] = {(B, Hkv, T, d)}; "
+                         f"got {tuple(k_cache.shape)} and {tuple(v_cache.shape)}")
+    if k_cache.device != q.device or v_cache.device != q.device:
+        raise TypeError("q, k_cache and v_cache must be on the same device")
+    if (lens.dtype != torch.int32 or lens.device != q.device or lens.dim() != 1
+            or lens.numel() != B or not lens.is_contiguous()):
+        raise TypeError(f"lens: expected a contiguous int32 [B] tensor on {q.device}")
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     if out is None:
         out = torch.empty((B, Hq, d), dtype=torch.bfloat16, device=q.device)
     o4 = out if out.dim() == 4 else out.unsqueeze(2)
+    _check_out("out", o4, (B, Hq, 1, d), torch.bfloat16, q.device)
     if lse is None:
         lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    _check_out("lse", lse, (B, Hq), torch.float32, q.device, contiguous=True)
     ws_bytes = lib.attn_decode_workspace_size(B, Hq, T, d, chunk)
+    if workspace is not None and (workspace.dtype != torch.uint8 or workspace.device != q.device):
+        raise TypeError(f"workspace: expected a uint8 tensor on {q.device}")
     if workspace is None or workspace.numel() < ws_bytes:
         workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=q.device)
     st = lib.attn_decode(_tensor4(q4), _tensor4(k_cache), _tensor4(v_cache),

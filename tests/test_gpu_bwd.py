@@ -8,12 +8,13 @@ gradients of the same bf16 inputs in fp64.
 Tolerance.  Each gradient entry is a sum over up to N keys (dQ) or N rows
 (dK, dV) of products in which the kernel rounds P and dS to bf16 (relative
 error 2^-9 each) before the fp32-accumulated MFMA, uses the bf16-rounded O
-in D = rowsum(dO * O), and rounds the result to bf16 (2^-9).  The error is
-therefore a few units of 2^-9 relative to the magnitude of the entries, not
-of their (possibly cancelling) sum, so it is measured against the largest
-entry of each tensor: max|g - g_ref| <= GRAD_TOL * max|g_ref| with
-GRAD_TOL = 2e-2, the forward's bar for O, which is also a max-abs bound on
-unit-scale values.  Where the exact gradient cancels to zero (a row with a
+in D = rowsum(dO * O) (2^-9), and rounds the result to bf16 (2^-9): four
+roundings of 2^-9, 7.8e-3 in all.  The error is therefore a few units of
+2^-9 relative to the magnitude of the entries, not of their (possibly
+cancelling) sum, so it is measured against the largest entry of each
+tensor: max|g - g_ref| <= GRAD_TOL * max|g_ref| with GRAD_TOL = 1e-2, just
+above those four roundings (measured: at most 5.5e-3 over every case
+here).  Where the exact gradient cancels to zero (a row with a
 single visible key has dS = 0) the fp32 residue of D - dP is left; GRAD_ABS
 = 1e-4 covers it (fp32 rounding, 2^-24, of sums of up to d unit-scale
 products).  Rows with no visible key and keys that no row sees get exactly
@@ -32,7 +33,7 @@ pytestmark = pytest.mark.gpu
 
 torch = pytest.importorskip("torch")
 
-GRAD_TOL = 2e-2
+GRAD_TOL = 1e-2
 GRAD_ABS = 1e-4
 
 
@@ -89,8 +90,11 @@ def run_case(ea, *, B, Hq, Hkv, N, d, seed, factor=1.0, causal=False, window=Non
     torch.cuda.synchronize()
     ref = oracle.bwd(q, k, v, dout, scale=scale, causal=causal, window=window,
                      softcap=softcap, **kw_ref)
-    return compare_grads((bf16_to_f64(dq), bf16_to_f64(dk), bf16_to_f64(dv)), ref,
+    errs = compare_grads((bf16_to_f64(dq), bf16_to_f64(dk), bf16_to_f64(dv)), ref,
                          lse.cpu().numpy(), label)
+    print(f"[case] {label}: max error / max|ref| dq {errs[0]:.2e} dk {errs[1]:.2e} dv {errs[2]:.2e}",
+          flush=True)
+    return errs
 
 
 @pytest.mark.parametrize("d", [64, 128])
@@ -167,3 +171,28 @@ def test_strided_layout_bshd(ea):
     torch.cuda.synchronize()
     ref = oracle.bwd(q, k, v, dout, scale=1.0 / math.sqrt(d), causal=True)
     compare_grads((bf16_to_f64(dq), bf16_to_f64(dk), bf16_to_f64(dv)), ref, lse.cpu().numpy(), "bshd")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("softcap", [None, 5.0])
+def test_unequal_kv_token_strides(ea, d, softcap):
+    # K stored [B, N, Hkv, d] (token stride Hkv*d) and V contiguous
+    # [B, Hkv, N, d] (token stride d): the dQ kernels that stream K and V
+    # tiles with separate offsets (the others share one set when the two
+    # token strides are equal)
+    B, Hq, Hkv, N = 2, 4, 2, 700
+    factor = 2.0 if softcap else 1.0
+    q, k, v, dout = _grad_inputs(581 + d, B, Hq, Hkv, N, d, factor)
+    print(f"[case] unequal K/V token strides B={B} Hq={Hq} Hkv={Hkv} N={N} d={d} "
+          f"softcap={softcap}", flush=True)
+    Q, V, G = to_dev(q), to_dev(v), to_dev(dout)
+    K = to_dev(np.ascontiguousarray(np.swapaxes(k, 1, 2))).transpose(1, 2)
+    assert K.stride(2) == Hkv * d and V.stride(2) == d
+    o, lse = ea.fwd(Q, K, V, causal=True, window=(400, 0), softcap=softcap)
+    dq, dk, dv = ea.bwd(Q, K, V, o, lse, G, causal=True, window=(400, 0), softcap=softcap)
+    torch.cuda.synchronize()
+    ref = oracle.bwd(q, k, v, dout, scale=1.0 / math.sqrt(d), causal=True, window=(400, 0),
+                     softcap=softcap)
+    errs = compare_grads((bf16_to_f64(dq), bf16_to_f64(dk), bf16_to_f64(dv)), ref,
+                         lse.cpu().numpy(), f"unequal strides d={d} cap={softcap}")
+    print(f"[case] relative errors dq/dk/dv {errs}", flush=True)

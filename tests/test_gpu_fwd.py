@@ -298,3 +298,96 @@ def test_long_sequence_sampled(ea):
     og = bf16_to_f64(o)[rows[:, 0], rows[:, 1], rows[:, 2]]
     lg = lse.cpu().numpy()[rows[:, 0], rows[:, 1], rows[:, 2]]
     compare(og, lg, ro, rl, "causal N=65536")
+
+
+# --------------------------------------------------------------------------
+# The running-max rescale of the plain kernels (no cap, no bias).  The
+# kernels keep a reference max per row and rescale O and l by
+# alpha = 2^(m_old - m_new) only when a row's max grows by more than 8
+# base-2 units over it; with N(0,1) inputs that almost never happens after
+# the first tile, so these inputs force it.
+# --------------------------------------------------------------------------
+def _ramp_inputs(seed, H, N, d):
+    """K rows scaled by 1 + j/16: a tile's largest score grows by about
+    ten base-2 units per 64-key tile, so the running max moves past the
+    threshold at almost every tile of a row."""
+    q, k, v, _ = gen.fwd_inputs(seed, 1, H, H, N, d)
+    kf = gen.f32_from_bf16_bits(k) * (1.0 + np.arange(N, dtype=np.float32) / 16.0)[None, None, :, None]
+    return q, gen.bf16_bits_from_f32(kf), v
+
+
+def _plateau_spike_inputs(seed, H, N, d):
+    """Every row sees a plateau of keys with scores near 0, then a few
+    'spike' keys (two at 250-251, three at 600-602, one at 900) whose
+    scores sit J nats higher, J = 7, 10.5 or 14 by row (i mod 3).  The
+    first spike a row meets lifts its max by J (10-20 base-2 units) while
+    the plateau keeps a sizeable share of the weight (about (i+1) : 2 e^J),
+    so a wrong alpha moves O by far more than the tolerance.  V carries 1
+    on the spike keys and 0 on the plateau (plus small noise), so O is the
+    spikes' share of the mass."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    u = np.ones(d, np.float32) / np.float32(np.sqrt(d))  # unit vector
+    amp = (1.0 + 0.5 * (np.arange(N) % 3)).astype(np.float32)
+    q = amp[None, None, :, None] * u * np.float32(np.sqrt(d)) \
+        + 0.05 * rng.standard_normal((1, H, N, d), dtype=np.float32)
+    level = np.zeros(N, np.float32)
+    spikes = [250, 251, 600, 601, 602, 900]
+    level[spikes] = 7.0
+    # score = scale * q.k = (amp * sqrt(d) u + e).(level u + e') / sqrt(d) ~ amp * level
+    k = level[None, None, :, None] * u + 0.05 * rng.standard_normal((1, H, N, d), dtype=np.float32)
+    vv = np.zeros((1, H, N, d), np.float32)
+    vv[:, :, spikes, :] = 1.0
+    vv += 0.1 * rng.standard_normal((1, H, N, d), dtype=np.float32)
+    return gen.bf16_bits_from_f32(q), gen.bf16_bits_from_f32(k), gen.bf16_bits_from_f32(vv)
+
+
+def _max_rises(q, k, scale, causal, thresh_log2=8.0):
+    """Per row, how many times the running max over ascending 64-key tiles
+    rises by more than thresh_log2 base-2 units over the reference max a
+    lazily rescaling kernel would keep (fp64, from the input scores)."""
+    qf = gen.f32_from_bf16_bits(q)[0].astype(np.float64)
+    kf = gen.f32_from_bf16_bits(k)[0].astype(np.float64)
+    s = np.einsum("hid,hjd->hij", qf, kf) * scale / np.log(2.0)
+    N = s.shape[-1]
+    if causal:
+        s = np.where(np.tril(np.ones((N, N), bool)), s, -np.inf)
+    H = s.shape[0]
+    ref = np.full((H, N), -np.inf)
+    rises = np.zeros((H, N), np.int64)
+    for t in range(0, N, 64):
+        mt = s[:, :, t:t + 64].max(axis=-1)
+        up = np.isfinite(ref) & (mt > ref + thresh_log2)
+        rises += up
+        ref = np.where(up | ~np.isfinite(ref), np.maximum(ref, mt), ref)
+    return rises
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("kind", ["ramp", "plateau_spikes"])
+def test_running_max_rescale(ea, kind, causal, d):
+    H, N = 2, 1000
+    scale = 1.0 / math.sqrt(d)
+    if kind == "ramp":
+        q, k, v = _ramp_inputs(70 + d, H, N, d)
+    else:
+        q, k, v = _plateau_spike_inputs(80 + d, H, N, d)
+    rises = _max_rises(q, k, scale, causal)
+    # the inputs do what they are for: most rows past the first spike or
+    # tile rescale mid-row, the ramp rows several times
+    late = rises[:, 700:]
+    assert (late >= 1).mean() > 0.9, kind
+    if kind == "ramp":
+        assert np.median(late) >= 5
+    print(f"[case] running-max rescale {kind} causal={causal} d={d}: "
+          f"rises per row median {np.median(rises):.0f}, max {rises.max()}", flush=True)
+    o, lse = ea.fwd(to_dev(q), to_dev(k), to_dev(v), causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    ro, rl = oracle.fwd(q, k, v, scale=scale, causal=causal)
+    eo, el = compare(bf16_to_f64(o), lse.cpu().numpy(), ro, rl, f"rescale {kind}")
+    print(f"[case] rescale {kind}: max|dO|={eo:.3e} max|dLSE|={el:.3e}", flush=True)
+    if kind == "plateau_spikes":
+        # the plateau's share of the weight is what a wrong alpha would get
+        # wrong: it must be substantial on the rows checked
+        share = ro[0, 0, 300:599, :].mean(axis=-1)
+        assert share.min() < 0.97 and share.max() > 0.5
