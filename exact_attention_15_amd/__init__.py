@@ -8,6 +8,6 @@ and streams, the kernels do all of the work.
 from .binding import (  # noqa: F401
     ATTN_MASK_CAUSAL, ATTN_MASK_DOCS, ATTN_MASK_NO_SKIP, ATTN_MASK_WINDOW,
     ATTN_MOD_ALIBI, ATTN_MOD_SOFTCAP, BLOCK_M, BLOCK_N, AttnError, MaskSpec, bwd, bwd_workspace_bytes,
-    decode, decode_workspace_bytes, fwd, fwd_fp8, fwd_varlen, fwd_varlen_workspace_bytes, library,
+    decode, decode_noalloc, decode_workspace_bytes, fwd, fwd_fp8, fwd_varlen, fwd_varlen_workspace_bytes, library,
     mask_build, mask_layout, mask_unpack, quantize_fp8,
 )

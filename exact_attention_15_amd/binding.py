@@ -84,6 +84,8 @@ def _load():
     lib.attn_decode_workspace_size.argtypes = [i32, i32, i32, i32, i32]
     lib.attn_decode.restype = i32
     lib.attn_decode.argtypes = [T, T, T, P, T, P, i32, i32, i32, i32, i32, i32, f32, P, sz, P]
+    lib.attn_decode_noalloc.restype = i32
+    lib.attn_decode_noalloc.argtypes = [T, T, T, P, T, P, i32, i32, i32, i32, i32, i32, f32, P]
     lib.attn_bwd_workspace_size.restype = sz
     lib.attn_bwd_workspace_size.argtypes = [SP, i32, i32, i32]
     lib.attn_bwd.restype = i32
@@ -479,6 +481,42 @@ def decode(q, k_cache, v_cache, lens, *, scale=None, chunk=1024, out=None, lse=N
                          lens.data_ptr(), _tensor4(o4), lse.data_ptr(), B, Hq, Hkv, T, d,
                          int(chunk), float(scale), workspace.data_ptr(), ws_bytes,
                          _stream(q.device))
+    _check(st)
+    return out, lse
+
+
+def decode_noalloc(q, k_cache, v_cache, lens, *, out, lse, scale=None, chunk=1024):
+    """``decode`` through attn_decode_noalloc: the chunk partials live in the
+    library's static per-GPU scratch, and nothing is allocated -- not here
+    either, so the caller passes ``out`` [B,Hq,d] bf16 and ``lse`` [B,Hq]
+    fp32.  Calls that may overlap on one GPU race on that scratch.
+    Returns (out, lse)."""
+    lib = _load()
+    for name, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache)):
+        _check_bf16(name, t)
+    if q.dim() not in (3, 4) or (q.dim() == 4 and q.shape[2] != 1):
+        raise ValueError(f"q: expected [B, Hq, d] or [B, Hq, 1, d], got {tuple(q.shape)}")
+    q4 = q if q.dim() == 4 else q.unsqueeze(2)
+    B, Hq, _, d = q4.shape
+    if k_cache.dim() != 4:
+        raise ValueError(f"k_cache: expected [B, Hkv, T, d], got {tuple(k_cache.shape)}")
+    Hkv, T = k_cache.shape[1], k_cache.shape[2]
+    if tuple(k_cache.shape) != (B, Hkv, T, d) or tuple(v_cache.shape) != (B, Hkv, T, d):
+        raise ValueError(f"k_cache and v_cache must both be [B, Hkv, T, d] = {(B, Hkv, T, d)}; "
+                         f"got {tuple(k_cache.shape)} and {tuple(v_cache.shape)}")
+    if k_cache.device != q.device or v_cache.device != q.device:
+        raise TypeError("q, k_cache and v_cache must be on the same device")
+    if (lens.dtype != torch.int32 or lens.device != q.device or lens.dim() != 1
+            or lens.numel() != B or not lens.is_contiguous()):
+        raise TypeError(f"lens: expected a contiguous int32 [B] tensor on {q.device}")
+    o4 = out if out.dim() == 4 else out.unsqueeze(2)
+    _check_out("out", o4, (B, Hq, 1, d), torch.bfloat16, q.device)
+    _check_out("lse", lse, (B, Hq), torch.float32, q.device, contiguous=True)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    st = lib.attn_decode_noalloc(_tensor4(q4), _tensor4(k_cache), _tensor4(v_cache), lens.data_ptr(),
+                                 _tensor4(o4), lse.data_ptr(), B, Hq, Hkv, T, d, int(chunk),
+                                 float(scale), _stream(q.device))
     _check(st)
     return out, lse
 

@@ -5,10 +5,23 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "common.h"
 
 using namespace exattn;
+
+// ---- static scratch of attn_decode_noalloc ----
+// The chunk partials (m, l, O) of attn_decode_noalloc live in this array
+// instead of a caller workspace.  Each GPU holds its own copy, at its own
+// address, from the library's load until the process ends.  In host code
+// the name `scratch` denotes a host-side stand-in, not device memory: the
+// device address is taken once per device with hipGetSymbolAddress (that
+// device current) and only that address is ever passed to a kernel.  Every
+// call on a GPU shares its copy; the combine reads only what the split of
+// the same call wrote, so nothing has to start at zero, and calls that
+// overlap on one GPU (different streams, or host threads) race.
+static __device__ __align__(256) uint8_t scratch[ATTN_DECODE_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -92,9 +105,98 @@ attn_mask_spec spec_or_default(const attn_mask_spec *spec) {
     return s;
 }
 
+// ---- decode: validation and launch shared by attn_decode and
+// attn_decode_noalloc ----
+attn_status decode_setup(const char *fn, attn_tensor q, attn_tensor k_cache, attn_tensor v_cache,
+                         const int32_t *lens, attn_tensor o, float *lse, int B, int Hq, int Hkv, int T, int d,
+                         int chunk, float scale, DecodeParams &p, size_t &need, size_t &off_l, size_t &off_o,
+                         bool &noop) {
+    noop = false;
+    if (B < 0 || T < 0) return fail(ATTN_ERR_INVALID, "%s: B=%d T=%d", fn, B, T);
+    if (Hq <= 0 || Hkv <= 0) return fail(ATTN_ERR_INVALID, "%s: Hq=%d Hkv=%d", fn, Hq, Hkv);
+    if (Hq % Hkv) return fail(ATTN_ERR_INVALID, "%s: Hq=%d is not a multiple of Hkv=%d", fn, Hq, Hkv);
+    if (Hq / Hkv > 16) return fail(ATTN_ERR_UNSUPPORTED, "%s: group size %d > 16", fn, Hq / Hkv);
+    if (d != 64 && d != 128) return fail(ATTN_ERR_UNSUPPORTED, "%s: head dim %d (supported: 64, 128)", fn, d);
+    if (chunk < 64 || chunk > 2048 || chunk % 64)
+        return fail(ATTN_ERR_UNSUPPORTED, "%s: chunk %d (multiple of 64 in [64, 2048])", fn, chunk);
+    if (!std::isfinite(scale) || !(scale > 0.f)) return fail(ATTN_ERR_INVALID, "%s: scale must be finite and > 0", fn);
+    if (B == 0) {
+        noop = true;
+        return ATTN_OK;
+    }
+    attn_status st;
+    if ((st = check_tensor(q, "q", false)) != ATTN_OK) return st;
+    if ((st = check_tensor(k_cache, "k_cache", true)) != ATTN_OK) return st;
+    if ((st = check_tensor(v_cache, "v_cache", true)) != ATTN_OK) return st;
+    if ((st = check_tensor(o, "o", false)) != ATTN_OK) return st;
+    if (k_cache.stride_n >= (int64_t(1) << 20) || v_cache.stride_n >= (int64_t(1) << 20))
+        return fail(ATTN_ERR_UNSUPPORTED, "%s: k/v cache token stride must be below 2^20 elements", fn);
+    if (!lens) return fail(ATTN_ERR_INVALID, "%s: null lens", fn);
+    if (!lse) return fail(ATTN_ERR_INVALID, "%s: null lse", fn);
+    const int nchunk = T > 0 ? (T + chunk - 1) / chunk : 1;
+    need = decode_ws_bytes(B, Hq, nchunk, d, &off_l, &off_o);
+    p.q = static_cast<const uint16_t *>(q.ptr);
+    p.k = static_cast<const uint16_t *>(k_cache.ptr);
+    p.v = static_cast<const uint16_t *>(v_cache.ptr);
+    p.o = static_cast<uint16_t *>(o.ptr);
+    p.lse = lse;
+    p.lens = lens;
+    p.q_sb = q.stride_b; p.q_sh = q.stride_h;
+    p.k_sb = k_cache.stride_b; p.k_sh = k_cache.stride_h; p.k_sn = k_cache.stride_n;
+    p.v_sb = v_cache.stride_b; p.v_sh = v_cache.stride_h; p.v_sn = v_cache.stride_n;
+    p.o_sb = o.stride_b; p.o_sh = o.stride_h;
+    p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.T = T; p.chunk = chunk; p.nchunk = nchunk;
+    p.scale_log2 = scale * 1.4426950408889634f;
+    return ATTN_OK;
+}
+
+attn_status decode_launch(const char *fn, DecodeParams &p, char *ws, size_t off_l, size_t off_o, int d,
+                          void *stream) {
+    p.part_m = reinterpret_cast<float *>(ws);
+    p.part_l = reinterpret_cast<float *>(ws + off_l);
+    p.part_o = reinterpret_cast<float *>(ws + off_o);
+    hipError_t e = launch_decode(p, d, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, fn);
+    return ATTN_OK;
+}
+
+constexpr int MAX_SCRATCH_DEVICES = 64;
+std::mutex g_scratch_mu;
+char *g_scratch_dev[MAX_SCRATCH_DEVICES] = {};
+
+// Device address of this library's scratch on the GPU that `stream` runs on
+// (the current device for the null stream).
+attn_status noalloc_scratch(void *stream, char **out) {
+    int dev = -1;
+    hipError_t e = stream ? hipStreamGetDevice(static_cast<hipStream_t>(stream), &dev) : hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "attn_decode_noalloc: device of the stream");
+    if (dev < 0 || dev >= MAX_SCRATCH_DEVICES)
+        return fail(ATTN_ERR_UNSUPPORTED, "attn_decode_noalloc: device %d (at most %d devices)", dev,
+                    MAX_SCRATCH_DEVICES);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_dev[dev]) {
+        int cur = -1;
+        if ((e = hipGetDevice(&cur)) != hipSuccess) return hip_fail(e, "attn_decode_noalloc: hipGetDevice");
+        if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess)
+            return hip_fail(e, "attn_decode_noalloc: hipSetDevice");
+        void *ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (cur != dev) {
+            hipError_t e2 = hipSetDevice(cur);
+            if (e == hipSuccess && e2 != hipSuccess) e = e2;
+        }
+        if (e != hipSuccess) return hip_fail(e, "attn_decode_noalloc: hipGetSymbolAddress of the scratch");
+        if (!ptr || !aligned16(ptr)) return fail(ATTN_ERR_HIP, "attn_decode_noalloc: bad scratch address");
+        g_scratch_dev[dev] = static_cast<char *>(ptr);
+    }
+    *out = g_scratch_dev[dev];
+    return ATTN_OK;
+}
+
 } // namespace
 
 extern "C" {
+
 
 const char *attn_status_string(attn_status s) {
     switch (s) {
@@ -453,51 +555,37 @@ size_t attn_decode_workspace_size(int B, int Hq, int T, int d, int chunk) {
 attn_status attn_decode(attn_tensor q, attn_tensor k_cache, attn_tensor v_cache, const int32_t *lens,
                         attn_tensor o, float *lse, int B, int Hq, int Hkv, int T, int d, int chunk,
                         float scale, void *workspace, size_t ws_bytes, void *stream) {
-    if (B < 0 || T < 0) return fail(ATTN_ERR_INVALID, "attn_decode: B=%d T=%d", B, T);
-    if (Hq <= 0 || Hkv <= 0) return fail(ATTN_ERR_INVALID, "attn_decode: Hq=%d Hkv=%d", Hq, Hkv);
-    if (Hq % Hkv) return fail(ATTN_ERR_INVALID, "attn_decode: Hq=%d is not a multiple of Hkv=%d", Hq, Hkv);
-    if (Hq / Hkv > 16) return fail(ATTN_ERR_UNSUPPORTED, "attn_decode: group size %d > 16", Hq / Hkv);
-    if (d != 64 && d != 128) return fail(ATTN_ERR_UNSUPPORTED, "attn_decode: head dim %d (supported: 64, 128)", d);
-    if (chunk < 64 || chunk > 2048 || chunk % 64)
-        return fail(ATTN_ERR_UNSUPPORTED, "attn_decode: chunk %d (multiple of 64 in [64, 2048])", chunk);
-    if (!std::isfinite(scale) || !(scale > 0.f)) return fail(ATTN_ERR_INVALID, "attn_decode: scale must be finite and > 0");
-    if (B == 0) return ATTN_OK;
-    attn_status st;
-    if ((st = check_tensor(q, "q", false)) != ATTN_OK) return st;
-    if ((st = check_tensor(k_cache, "k_cache", true)) != ATTN_OK) return st;
-    if ((st = check_tensor(v_cache, "v_cache", true)) != ATTN_OK) return st;
-    if ((st = check_tensor(o, "o", false)) != ATTN_OK) return st;
-    if (k_cache.stride_n >= (int64_t(1) << 20) || v_cache.stride_n >= (int64_t(1) << 20))
-        return fail(ATTN_ERR_UNSUPPORTED, "attn_decode: k/v cache token stride must be below 2^20 elements");
-    if (!lens) return fail(ATTN_ERR_INVALID, "attn_decode: null lens");
-    if (!lse) return fail(ATTN_ERR_INVALID, "attn_decode: null lse");
-    const int nchunk = T > 0 ? (T + chunk - 1) / chunk : 1;
-    size_t off_l = 0, off_o = 0;
-    const size_t need = decode_ws_bytes(B, Hq, nchunk, d, &off_l, &off_o);
+    DecodeParams p;
+    size_t need = 0, off_l = 0, off_o = 0;
+    bool noop = false;
+    attn_status st = decode_setup("attn_decode", q, k_cache, v_cache, lens, o, lse, B, Hq, Hkv, T, d, chunk,
+                                  scale, p, need, off_l, off_o, noop);
+    if (st != ATTN_OK || noop) return st;
     if (!workspace || ws_bytes < need)
         return fail(ATTN_ERR_WORKSPACE, "attn_decode: workspace needs %zu bytes, got %zu", need,
                     workspace ? ws_bytes : size_t(0));
     if (!aligned16(workspace)) return fail(ATTN_ERR_INVALID, "attn_decode: workspace not 16-byte aligned");
+    return decode_launch("attn_decode", p, static_cast<char *>(workspace), off_l, off_o, d, stream);
+}
+
+attn_status attn_decode_noalloc(attn_tensor q, attn_tensor k_cache, attn_tensor v_cache, const int32_t *lens,
+                                attn_tensor o, float *lse, int B, int Hq, int Hkv, int T, int d, int chunk,
+                                float scale, void *stream) {
     DecodeParams p;
-    p.q = static_cast<const uint16_t *>(q.ptr);
-    p.k = static_cast<const uint16_t *>(k_cache.ptr);
-    p.v = static_cast<const uint16_t *>(v_cache.ptr);
-    p.o = static_cast<uint16_t *>(o.ptr);
-    p.lse = lse;
-    p.lens = lens;
-    p.q_sb = q.stride_b; p.q_sh = q.stride_h;
-    p.k_sb = k_cache.stride_b; p.k_sh = k_cache.stride_h; p.k_sn = k_cache.stride_n;
-    p.v_sb = v_cache.stride_b; p.v_sh = v_cache.stride_h; p.v_sn = v_cache.stride_n;
-    p.o_sb = o.stride_b; p.o_sh = o.stride_h;
-    p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.T = T; p.chunk = chunk; p.nchunk = nchunk;
-    p.scale_log2 = scale * 1.4426950408889634f;
-    char *ws = static_cast<char *>(workspace);
-    p.part_m = reinterpret_cast<float *>(ws);
-    p.part_l = reinterpret_cast<float *>(ws + off_l);
-    p.part_o = reinterpret_cast<float *>(ws + off_o);
-    hipError_t e = launch_decode(p, d, static_cast<hipStream_t>(stream));
-    if (e != hipSuccess) return hip_fail(e, "attn_decode");
-    return ATTN_OK;
+    size_t need = 0, off_l = 0, off_o = 0;
+    bool noop = false;
+    attn_status st = decode_setup("attn_decode_noalloc", q, k_cache, v_cache, lens, o, lse, B, Hq, Hkv, T, d,
+                                  chunk, scale, p, need, off_l, off_o, noop);
+    if (st != ATTN_OK || noop) return st;
+    if (need > ATTN_DECODE_NOALLOC_SCRATCH_BYTES)
+        return fail(ATTN_ERR_WORKSPACE,
+                    "attn_decode_noalloc: the chunk partials need %zu bytes, more than the %zu-byte static "
+                    "scratch (B * Hq * ceil(T / chunk) * (d + 2) * 4 bytes plus alignment); use attn_decode "
+                    "with a workspace",
+                    need, size_t(ATTN_DECODE_NOALLOC_SCRATCH_BYTES));
+    char *ws = nullptr;
+    if ((st = noalloc_scratch(stream, &ws)) != ATTN_OK) return st;
+    return decode_launch("attn_decode_noalloc", p, ws, off_l, off_o, d, stream);
 }
 
 } // extern "C"

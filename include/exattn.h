@@ -198,6 +198,30 @@ attn_status attn_decode(attn_tensor q, attn_tensor k_cache, attn_tensor v_cache,
                         void *workspace, size_t ws_bytes, void *stream);
 
 /*
+ * attn_decode without a workspace, for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops and harnesses
+ * that forbid hipMalloc.  The chunk partials live in a static device array
+ * of ATTN_DECODE_NOALLOC_SCRATCH_BYTES inside the library, one copy per GPU,
+ * held from the library's load until the process ends.  The call makes no
+ * allocation of any kind.
+ *   Arguments, layouts, results and the other errors: as attn_decode (the
+ *   caller still owns q, the caches, lens, o and lse).
+ *   The partials need attn_decode_workspace_size(B, Hq, T, d, chunk) bytes;
+ *   a call needing more than ATTN_DECODE_NOALLOC_SCRATCH_BYTES returns
+ *   ATTN_ERR_WORKSPACE and enqueues nothing (use attn_decode then).
+ *   Every call on one GPU shares that GPU's scratch: calls that may overlap
+ *   on the same GPU (different streams or host threads) race; calls on one
+ *   stream are ordered and safe.  Nothing in the scratch needs clearing
+ *   between calls.  The first call on a device looks up that device's
+ *   scratch address (hipGetSymbolAddress); ATTN_ERR_HIP if that fails.
+ */
+#define ATTN_DECODE_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+attn_status attn_decode_noalloc(attn_tensor q, attn_tensor k_cache, attn_tensor v_cache,
+                                const int32_t *lens, attn_tensor o, float *lse, int B,
+                                int Hq, int Hkv, int T, int d, int chunk, float scale,
+                                void *stream);
+
+/*
  * Backward of attn_fwd: the gradients dQ, dK, dV of a loss given its
  * gradient dO with respect to O.  The probabilities are recomputed tile by
  * tile from lse instead of being stored (youngju.dev "FlashAttention 논문

@@ -34,7 +34,7 @@ def test_header_declares_the_boundary():
               "attn_bwd", "attn_bwd_workspace_size",
               "attn_fwd_varlen", "attn_fwd_varlen_workspace_size",
               "attn_fwd_fp8", "attn_quantize_fp8", "attn_quantize_fp8_workspace_size",
-              "attn_status_string", "attn_last_error"):
+              "attn_decode_noalloc", "attn_status_string", "attn_last_error"):
         assert n in names
 
 
@@ -101,6 +101,28 @@ def test_fwd_rejects_bad_specs(lib):
         st = lib.attn_fwd(t, t, t, t, ctypes.c_void_p(16), 1, 2, 2, 8, 128, ctypes.byref(spec),
                           ctypes.c_float(0.1), None, None, 0, None)
         assert st == b.ATTN_ERR_INVALID
+
+
+def test_decode_noalloc_validation_before_launch(lib):
+    # the allocation-free decode validates like attn_decode and rejects
+    # partials larger than its static scratch before any HIP call
+    from exact_attention_15_amd import binding as b
+    t = _t(16, 0, 0, 128)
+    limit = 16 << 20
+
+    def call(B=2, Hq=8, Hkv=2, T=4096, d=128, chunk=1024, lens=16):
+        return lib.attn_decode_noalloc(t, t, t, lens, t, ctypes.c_void_p(16), B, Hq, Hkv, T, d, chunk,
+                                       ctypes.c_float(0.1), None)
+    assert call(d=80) == b.ATTN_ERR_UNSUPPORTED
+    assert call(Hq=6, Hkv=4) == b.ATTN_ERR_INVALID
+    assert call(chunk=1000) == b.ATTN_ERR_UNSUPPORTED
+    assert call(lens=None) == b.ATTN_ERR_INVALID
+    assert call(B=0) == b.ATTN_OK
+    # the decode workload's partials fit; twice its cache length does not
+    assert lib.attn_decode_workspace_size(16, 32, 32768, 128, 1024) <= limit
+    assert lib.attn_decode_workspace_size(16, 32, 65536, 128, 1024) > limit
+    assert call(B=16, Hq=32, Hkv=8, T=65536) == b.ATTN_ERR_WORKSPACE
+    assert b"static" in lib.attn_last_error()
 
 
 def test_decode_validation_before_launch(lib):
