@@ -18,10 +18,12 @@
 // k-step in byte order, for P V it is the accumulator's key order.
 //
 // Scales: S = s_raw * sq(row block) * sk(key tile) * scale, folded into the
-// exponent's FMA (per lane and tile).  The reference max is kept exact (no
-// lazy slack), so p <= 1 and p * 256 = 2^(s - m + 8) uses the E4M3 range
-// down to 2^-17 of the row max; O = acc * sv / l, with acc and l both in
-// units of 256 p and l summed from the unrounded values.
+// exponent's FMA (per lane and tile).  The reference max m moves lazily: it
+// trails a row's running max by at most 2^RESCALE8 = 4 (it is raised only
+// when a tile's max exceeds it by more), so p = 2^(s - m) <= 4 and the P V
+// operand p * 2^6 = 2^(s - m + 6) stays <= 256, within E4M3's range;
+// O = acc * sv / l, with acc and l both in units of 2^6 p and l summed from
+// the unrounded values.
 #include "tile.h"
 
 namespace exattn {

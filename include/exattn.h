@@ -113,7 +113,15 @@ attn_status attn_mask_build(const attn_mask_spec *spec, int B, int N, void *out,
                             size_t bytes, void *stream);
 
 /*
- * Forward attention (prefill, Nq = Nk = N).
+ * Forward attention (prefill, Nq = Nk = N): O = softmax(Q K^T * scale) V
+ * per (batch row, query head), computed tile by tile with a running row
+ * max and sum so that no score or probability matrix is stored
+ * (youngju.dev "FlashAttention 논문 분석", sections "수학적 정의",
+ * "Online Softmax와 블록 단위 누적" and "알고리즘 의사코드"; the
+ * FlashAttention-2 section for normalising once at the end and for the
+ * grid over query tiles).  Masks and score mods per attn_mask_spec
+ * (it-trends-board "PyTorch FlexAttention 도입 분석", section 2; aegloslab
+ * "3.7 어텐션 II", section 3.7.5).
  *   q [B,Hq,N,d], k and v [B,Hkv,N,d]: bf16 inputs; query head h reads KV
  *     head h / (Hq/Hkv) (grouped-query attention, no K/V copies).
  *   o [B,Hq,N,d]: bf16 output, normalised (O = P V with rows of P summing
@@ -295,9 +303,23 @@ attn_status attn_fwd_fp8(attn_tensor q, attn_tensor k, attn_tensor v, const floa
                          float scale, const void *block_mask, void *workspace, size_t ws_bytes,
                          void *stream);
 
-/* Static description of a status code. */
+/*
+ * Errors.  Unsupported input is refused with a status and a message that
+ * names what is unsupported (head dim, group size, layout, alignment), and
+ * nothing runs in its place: the pages' troubleshooting material shows the
+ * same convention (an exception that names the unsupported architecture or
+ * tensor shape: youngju.dev "FlashAttention 논문 분석", section "트러블슈팅:
+ * 실패 사례와 복구", cases 1 and 2) and names the silent fall back to a
+ * slower N x N path as the most common hidden loss (aegloslab "3.7 어텐션
+ * II", sections 3.7.3 and 3.7.9).
+ *
+ * attn_status_string: a static, never-null description of a status code
+ *   ("unknown status" for values outside the enum).
+ * attn_last_error: the message of the calling thread's most recent non-OK
+ *   status ("" if there was none); thread-local storage owned by the
+ *   library, valid until that thread's next call.
+ */
 const char *attn_status_string(attn_status status);
-/* Detail for the calling thread's most recent non-OK status ("" if none). */
 const char *attn_last_error(void);
 
 #ifdef __cplusplus
