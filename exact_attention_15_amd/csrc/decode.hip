@@ -29,7 +29,7 @@ typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
 constexpr float LN2_D = 0.6931471805599453f;
 constexpr int MAX_CHUNK = 2048;
-constexpr int K_AHEAD = 3; // 16-key K groups in flight per wave
+constexpr int K_AHEAD = 4; // 16-key K groups in flight per wave
 constexpr int V_PAIRS = 4; // V row pairs (two 16-byte loads each) in flight per lane
 
 
@@ -51,15 +51,15 @@ __device__ __forceinline__ float wave_sum(float x) {
 // whatever the mix of lengths; a grid indexed directly by (chunk, head, b)
 // would give the low XCDs up to one extra chunk per (b, head).  Returns false
 // for the ids past the last item.  Wave-uniform; lens is scanned 64 rows at a
-// time with a wave prefix sum.
-__device__ __forceinline__ bool decode_item(const DecodeParams &p, int &b, int &g, int &c) {
+// time with a wave prefix sum, which also gives the row's length.
+__device__ __forceinline__ bool decode_item(const DecodeParams &p, int &b, int &g, int &c, int &len_b) {
     int i = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
     const int lane = threadIdx.x & 63;
     for (int b0 = 0; b0 < p.B; b0 += 64) {
         const int bb = b0 + lane;
-        int nc = 0;
+        int nc = 0, len = 0;
         if (bb < p.B) {
-            int len = p.lens[bb];
+            len = p.lens[bb];
             len = len < 0 ? 0 : (len > p.T ? p.T : len);
             nc = (len + p.chunk - 1) / p.chunk;
         }
@@ -78,6 +78,7 @@ __device__ __forceinline__ bool decode_item(const DecodeParams &p, int &b, int &
             b = __builtin_amdgcn_readfirstlane(b0 + l);
             g = __builtin_amdgcn_readfirstlane(j / ncl);
             c = __builtin_amdgcn_readfirstlane(j % ncl);
+            len_b = __builtin_amdgcn_readfirstlane(__shfl(len, l)); // clamped into [0, T]
             return true;
         }
         i -= total;
@@ -103,10 +104,8 @@ __global__ __launch_bounds__(64 * decode_max_waves<G>()) void k_decode_split(Dec
     constexpr int KP = 2 * KPI;  // keys per V iteration (each lane takes a pair)
     extern __shared__ __attribute__((aligned(16))) float sm[];
 
-    int b, g, c;
-    if (!decode_item(p, b, g, c)) return;
-    int len = p.lens[b];
-    len = len < 0 ? 0 : (len > p.T ? p.T : len);
+    int b, g, c, len;
+    if (!decode_item(p, b, g, c, len)) return;
     const int k0 = c * p.chunk;
     const int nk = min(p.chunk, len - k0);
 
@@ -137,9 +136,9 @@ __global__ __launch_bounds__(64 * decode_max_waves<G>()) void k_decode_split(Dec
     if (nkw > 0) {
         // ---- pass 1: scores S = Q K^T, 16 keys per MFMA group ----
         // A operand: lane l holds query row l%16 (zero beyond the group), and
-        // for k-step s the 8 elements [(D/4)*(l/16) + 8s, +8).  B operand:
-        // lane l holds key l%16 of the 16-key group with the same element
-        // ranges, so each lane reads D/2 contiguous bytes of one K row.
+        // for k-step s the 8 elements [32s + 8(l/16), +8).  B operand: lane l
+        // holds key l%16 of the 16-key group with the same element ranges, so
+        // each load instruction reads 64 contiguous bytes of each of 16 rows.
         const int r16 = lane & 15, g4 = lane >> 4;
         bf16x8_t qa[KS];
         {
@@ -147,15 +146,15 @@ __global__ __launch_bounds__(64 * decode_max_waves<G>()) void k_decode_split(Dec
             const uint16_t *qrow = p.q + b * p.q_sb + int64_t(g * group + (ok ? r16 : 0)) * p.q_sh;
 #pragma unroll
             for (int s = 0; s < KS; ++s) {
-                const u32x4_t x = *reinterpret_cast<const u32x4_t *>(qrow + (D / 4) * g4 + 8 * s);
+                const u32x4_t x = *reinterpret_cast<const u32x4_t *>(qrow + 32 * s + 8 * g4);
                 qa[s] = ok ? __builtin_bit_cast(bf16x8_t, x) : bf16x8_t{};
             }
         }
         auto kload = [&](int grp, u32x4_t *dst) {
             const int key = min(grp * 16 + r16, nkw - 1);
-            const uint16_t *src = kbase + int64_t(key) * p.k_sn + (D / 4) * g4;
+            const uint16_t *src = kbase + int64_t(key) * p.k_sn + 8 * g4;
 #pragma unroll
-            for (int s = 0; s < KS; ++s) dst[s] = *reinterpret_cast<const u32x4_t *>(src + 8 * s);
+            for (int s = 0; s < KS; ++s) dst[s] = *reinterpret_cast<const u32x4_t *>(src + 32 * s);
         };
         const int ngroups = (nkw + 15) >> 4;
         const int ngroups_pad = (ngroups + K_AHEAD - 1) / K_AHEAD * K_AHEAD;
@@ -324,14 +323,19 @@ __global__ __launch_bounds__(64 * decode_max_waves<G>()) void k_decode_split(Dec
 }
 
 // One workgroup of D threads per (query head, b): merge the chunk partials.
-// The chunks are read in batches of COMBINE_BATCH whose loads are all issued
-// before any is used (rows past the last chunk are clamped and weighted 0),
-// and the running max / sum / output are rescaled once per batch, so a
-// (b, head) with up to COMBINE_BATCH chunks costs one round trip to memory.
+// The chunks are taken in batches of COMBINE_BATCH.  Every thread issues the
+// loads of its output element for the whole batch at once (rows past the
+// last chunk are clamped and weighted 0) while the first wave loads the
+// batch's maxima and sums, one chunk per lane, reduces them and leaves the
+// chunk weights exp(m_c - M) in LDS; the running max / sum / output are
+// rescaled once per batch, so a (b, head) with up to COMBINE_BATCH chunks
+// costs one round trip to memory and each thread makes COMBINE_BATCH loads.
 constexpr int COMBINE_BATCH = 32;
 template <int D>
 __global__ __launch_bounds__(D) void k_decode_combine(DecodeParams p) {
-    const int h = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
+    __shared__ float w_sh[COMBINE_BATCH];
+    __shared__ float stat_sh[2]; // the batch's new running max and weighted sum
+    const int h = blockIdx.x, b = blockIdx.y, d = threadIdx.x, lane = d & 63;
     int len = p.lens[b];
     len = len < 0 ? 0 : (len > p.T ? p.T : len);
     const int nch = (len + p.chunk - 1) / p.chunk;
@@ -339,29 +343,34 @@ __global__ __launch_bounds__(D) void k_decode_combine(DecodeParams p) {
     uint16_t *orow = p.o + b * p.o_sb + h * p.o_sh;
     float M = -INFINITY, L = 0.f, acc = 0.f;
     for (int c0 = 0; c0 < nch; c0 += COMBINE_BATCH) {
-        float mv[COMBINE_BATCH], lv[COMBINE_BATCH], ov[COMBINE_BATCH];
+        float ov[COMBINE_BATCH];
 #pragma unroll
-        for (int j = 0; j < COMBINE_BATCH; ++j) {
-            const int c = min(c0 + j, nch - 1);
-            mv[j] = p.part_m[base + c];
-            lv[j] = p.part_l[base + c];
-            ov[j] = p.part_o[(base + c) * D + d];
+        for (int j = 0; j < COMBINE_BATCH; ++j) ov[j] = p.part_o[(base + min(c0 + j, nch - 1)) * D + d];
+        if (d < 64) {
+            const bool ok = lane < COMBINE_BATCH && c0 + lane < nch;
+            const int cc = ok ? c0 + lane : 0;
+            const float mv = ok ? p.part_m[base + cc] : -INFINITY;
+            const float lv = ok ? p.part_l[base + cc] : 0.f;
+            // a chunk holds at least one key, so its max is finite unless
+            // scores overflowed
+            const float Mb = fmaxf(M, wave_max(mv));
+            const float w = ok ? __builtin_amdgcn_exp2f(mv - Mb) : 0.f;
+            if (lane < COMBINE_BATCH) w_sh[lane] = w;
+            const float Lb = wave_sum(w * lv);
+            if (lane == 0) {
+                stat_sh[0] = Mb;
+                stat_sh[1] = Lb;
+            }
         }
-        float Mb = M;
-#pragma unroll
-        for (int j = 0; j < COMBINE_BATCH; ++j)
-            if (c0 + j < nch) Mb = fmaxf(Mb, mv[j]);
-        // a chunk holds at least one key, so Mb is finite unless scores overflowed
+        __syncthreads();
+        const float Mb = stat_sh[0];
         const float r = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(M - Mb);
-        L *= r;
+        L = __builtin_fmaf(L, r, stat_sh[1]);
         acc *= r;
 #pragma unroll
-        for (int j = 0; j < COMBINE_BATCH; ++j) {
-            const float w = c0 + j < nch ? __builtin_amdgcn_exp2f(mv[j] - Mb) : 0.f;
-            L += w * lv[j];
-            acc += w * ov[j];
-        }
+        for (int j = 0; j < COMBINE_BATCH; ++j) acc = __builtin_fmaf(w_sh[j], ov[j], acc);
         M = Mb;
+        __syncthreads(); // the next batch rewrites the weights
     }
     const float o = L > 0.f ? acc / L : 0.f;
     __bf16 ob = (__bf16)o;
