@@ -10,7 +10,8 @@ whole forward path.  FLOPs count 4*d per visible (query, key) pair.
 The same JSON line also carries:
   roofline      the forward kernel alone (prebuilt block mask), timed with
                 HIP events on the stream it is launched on, against the bf16
-                dense MFMA peak;
+                dense MFMA peak; every prefill workload in ``configs`` carries
+                its own block of the same form;
   decode        split-KV decode (split + combine kernels) on B=16, 32 query
                 heads over 8 KV heads, T=32768, lens U[1024, 32768], chunk
                 1024: HBM GB/s of the algorithmic K/V bytes, against 8 TB/s;
@@ -19,10 +20,10 @@ The same JSON line also carries:
                 products per visible pair), against the bf16 MFMA peak;
   varlen        attn_fwd_varlen on the GQA document workload packed into
                 [B*N, H, d] with its documents as the sequences (config 7,
-                run with config 4);
+                on config 4's inputs);
   alibi         the forward kernel on the headline workload with the ALiBi
-                distance bias, slopes 2^(-8(h+1)/H) (config 8, run with
-                config 2);
+                distance bias, slopes 2^(-8(h+1)/H) (config 8, on config 2's
+                inputs);
   fp8           the FP8 forward kernel on the headline workload's inputs,
                 Q and K rotated by a random-sign Hadamard matrix and all
                 three block-quantized to E4M3 (config 9): TFLOP/s against
@@ -33,6 +34,10 @@ The same JSON line also carries:
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
                        [--configs 1,2,3,4,5,6,7,8,9]
+
+Configs 7, 8 and 9 generate the inputs of the workload they derive from but
+time only themselves unless that workload is listed too, so that a profiler
+run can hold one workload's dispatches alone.
 """
 from __future__ import annotations
 
@@ -60,7 +65,7 @@ HBM_PEAK_GBS = 8000.0           # MI355X HBM3E
 BWD_FLOP_FACTOR = 2.5
 CSRC = os.path.join(ROOT, "exact_attention_15_amd", "csrc")
 
-# HBM bytes per launch of the dominant kernels, from two rocprofv3 --pmc runs
+# HBM bytes per launch, per workload, from two rocprofv3 --pmc runs
 # (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch) of this script, each scaled
 # by what the same counter reads for a device copy of known size
 # (--calibrate-copy): FETCH_SIZE counts half of the bytes a copy reads,
@@ -68,30 +73,65 @@ CSRC = os.path.join(ROOT, "exact_attention_15_amd", "csrc")
 # source it was taken on; if the sources' sha256 differs it is reported as
 # null (stale).  The build script is hashed with the sources, since its
 # per-file compiler flags change the kernels' machine code too.
+_FWD_SRC = ["fwd.hip", "tile.h", "common.h", "../build.py"]
 MEASURED_TRAFFIC = {
-    # kernel: (sources, sha256 of their concatenation, bytes per launch, summary)
-    "k_attn_fwd_d128": (
+    # workload: (kernels, sources, sha256 of their concatenation, bytes per launch, summary)
+    "causal_b8_h32_n4096_d128": (
+        "k_attn_fwd_d128",
         ["fwd.hip", "tile.h", "common.h", "../build.py"],
         "7c27c81005dd02fbb2328209dc0787ada9f819f8056620fb11d9e037971f5ca8",
-        1118222921,
+        1117978228,
         "profiles/k_attn_fwd_d128_causal_b8_h32_n4096_d128.md"),
-    "k_decode_split": (
-        ["decode.hip", "common.h", "../build.py"],
-        "7910928147fecd0f6b97f37b6102d5f5a04cecb2afd912e8a46d7ce2318c62f0",
-        958343927,
-        "profiles/k_decode_split_decode_b16_gqa32x8_t32768_d128.md"),
-    # all kernels of one attn_bwd call (mask_kv, prep, dQ, dK/dV)
-    "attn_bwd_d128": (
-        ["bwd.hip", "tile.h", "common.h", "../build.py"],
-        "5e9a5362a2438cd9eda905d30a73d21bb5017cf46e3f8e5ae6ed5714cc8947e1",
-        3603356191,
-        "profiles/k_bwd_d128_causal_b8_h32_n4096_d128.md"),
-    "k_attn_fwd8_d128": (
+    "window1024_softcap50_b4_h32_n16384_d128": (
+        "k_attn_fwd_d128_softcap",
+        ["fwd.hip", "tile.h", "common.h", "../build.py"],
+        "7c27c81005dd02fbb2328209dc0787ada9f819f8056620fb11d9e037971f5ca8",
+        2498594933,
+        "profiles/k_attn_fwd_d128_softcap_window1024_softcap50_b4_h32_n16384_d128.md"),
+    "gqa32x8_docs_causal_b2_n8192_d128": (
+        "k_attn_fwd_d128",
+        ["fwd.hip", "tile.h", "common.h", "../build.py"],
+        "7c27c81005dd02fbb2328209dc0787ada9f819f8056620fb11d9e037971f5ca8",
+        399013389,
+        "profiles/k_attn_fwd_d128_gqa32x8_docs_causal_b2_n8192_d128.md"),
+    "varlen_gqa32x8_docs_causal_b2_n8192_d128": (
+        "k_mask_tiles + k_mask_order + k_attn_fwd_d128",
+        ["fwd.hip", "tile.h", "common.h", "../build.py", "mask.hip"],
+        "85e0cd12bee21745fba15a5185d99a3081469cc4de417a0dd176425bceb9bbb3",
+        607866621,
+        "profiles/attn_fwd_varlen_gqa32x8_docs_b2_n8192_d128.md"),
+    "alibi_causal_b8_h32_n4096_d128": (
+        "k_attn_fwd_d128_alibi",
+        ["fwd.hip", "tile.h", "common.h", "../build.py"],
+        "7c27c81005dd02fbb2328209dc0787ada9f819f8056620fb11d9e037971f5ca8",
+        1116309633,
+        "profiles/k_attn_fwd_d128_alibi_causal_b8_h32_n4096_d128.md"),
+    "fp8_causal_b8_h32_n4096_d128": (
+        "k_attn_fwd8_d128",
         ["fwd8.hip", "tile.h", "common.h", "../build.py"],
-        "bfb09f8e45c098f3c84a9e6cbec5074081dbc9bbb8a9e31c1511caa4af200e05",
-        679384764,
+        "ab3c5295ee176b12ec79b86e39f5e07cffab2d8ba234a0c4e8e1727156858793",
+        679392187,
         "profiles/k_attn_fwd8_d128_causal_b8_h32_n4096_d128.md"),
+    "decode_b16_gqa32x8_t32768_d128_chunk1024": (
+        "k_decode_split + k_decode_combine",
+        ["decode.hip", "common.h", "../build.py"],
+        "c3772f0195e9a3d4a50501737135247e92e96facd1467ab377dc3f2ee413cb07",
+        961770538,
+        "profiles/k_decode_split_decode_b16_gqa32x8_t32768_d128.md"),
+    "bwd_causal_b8_h32_n4096_d128": (
+        "all kernels of one attn_bwd call",
+        ["bwd.hip", "tile.h", "common.h", "mask.hip", "../build.py"],
+        "d19dd1e65f641f7a39c1039019b9e98b7d7a6f6dd30caa6c903bf18106bc2596",
+        3610043247,
+        "profiles/k_bwd_d128_causal_b8_h32_n4096_d128.md"),
 }
+
+# Forward kernel that each prefill workload runs.
+FWD_KERNEL = {1: "k_attn_fwd_d64", 2: "k_attn_fwd_d128", 3: "k_attn_fwd_d128_softcap",
+              4: "k_attn_fwd_d128"}
+# Workloads timed on another workload's inputs: varlen packs workload 4,
+# ALiBi and FP8 run on workload 2's Q, K, V.
+DERIVED_FROM = {7: 4, 8: 2, 9: 2}
 
 
 def sources_sha256(names) -> str:
@@ -103,14 +143,19 @@ def sources_sha256(names) -> str:
     return h.hexdigest()
 
 
-def measured_traffic(kernel: str):
-    """Counter-measured HBM bytes per launch of ``kernel`` or None if there is
-    no figure for the current source."""
-    entry = MEASURED_TRAFFIC.get(kernel)
+def measured_traffic(workload: str):
+    """Counter-measured HBM bytes per launch on ``workload`` or None if there
+    is no figure for the current source."""
+    entry = MEASURED_TRAFFIC.get(workload)
     if entry is None:
         return None
-    names, digest, nbytes, _ = entry
+    _, names, digest, nbytes, _ = entry
     return nbytes if sources_sha256(names) == digest else None
+
+
+def mfma_roofline(tflops: float, peak: float, workload: str, **extra):
+    return dict({"bound": "mfma", "achieved": round(tflops, 2), "peak": peak, "unit": "TFLOP/s",
+                 "frac": round(tflops / peak, 4), "traffic": measured_traffic(workload)}, **extra)
 
 
 # ---------------------------------------------------------------------------
@@ -472,82 +517,81 @@ def main(argv=None):
     varlen_res = None
     alibi_res = None
     fp8_res = None
-    for cid in cfg_ids:
-        if cid in (5, 6, 7, 8, 9):
-            continue
+    bases = sorted({c for c in cfg_ids if c in FWD_KERNEL}
+                   | {DERIVED_FROM[c] for c in cfg_ids if c in DERIVED_FROM})
+    for cid in bases:
         print(f"[bench] config {cid}: generating inputs", file=sys.stderr, flush=True)
         w = fwd_workload(cid, dev)
-        r = bench_fwd(ea, w, args.steps, args.warmup)
         c = w["cfg"]
-        results[c["name"]] = {
-            "ms_step": round(r["ms_step"], 4), "ms_kernel": round(r["ms_kernel"], 4),
-            "ms_mask_build": round(r["ms_mask_build"], 4),
-            "kernel_median_ms": round(r["dist"]["median_ms"], 4),
-            "kernel_min_ms": round(r["dist"]["min_ms"], 4),
-            "kernel_p90_ms": round(r["dist"]["p90_ms"], 4),
-            "tflops_step": round(r["tflops_step"], 2),
-            "tflops_kernel": round(r["tflops_kernel"], 2),
-            "frac_mfma_peak": round(r["tflops_kernel"] / MFMA_BF16_PEAK_TFLOPS, 4),
-            "flops": w["flops"], "visible_pairs_per_head": w["pairs_per_head"],
-        }
-        print(f"[bench] config {cid} {c['name']}: {r['ms_kernel']:.3f} ms kernel, "
-              f"{r['tflops_kernel']:.1f} TFLOP/s", file=sys.stderr, flush=True)
+        r = None
+        if cid in cfg_ids:
+            r = bench_fwd(ea, w, args.steps, args.warmup)
+            results[c["name"]] = {
+                "ms_step": round(r["ms_step"], 4), "ms_kernel": round(r["ms_kernel"], 4),
+                "ms_mask_build": round(r["ms_mask_build"], 4),
+                "kernel_median_ms": round(r["dist"]["median_ms"], 4),
+                "kernel_min_ms": round(r["dist"]["min_ms"], 4),
+                "kernel_p90_ms": round(r["dist"]["p90_ms"], 4),
+                "tflops_step": round(r["tflops_step"], 2),
+                "tflops_kernel": round(r["tflops_kernel"], 2),
+                "frac_mfma_peak": round(r["tflops_kernel"] / MFMA_BF16_PEAK_TFLOPS, 4),
+                "flops": w["flops"], "visible_pairs_per_head": w["pairs_per_head"],
+                "roofline": mfma_roofline(r["tflops_kernel"], MFMA_BF16_PEAK_TFLOPS, c["name"],
+                                          kernel=FWD_KERNEL[cid]),
+            }
+            print(f"[bench] config {cid} {c['name']}: {r['ms_kernel']:.3f} ms kernel, "
+                  f"{r['tflops_kernel']:.1f} TFLOP/s", file=sys.stderr, flush=True)
         if cid == 4 and 7 in cfg_ids:
             rv = bench_varlen(ea, w, args.steps, args.warmup)
+            name = "varlen_" + c["name"]
             varlen_res = {
-                "workload": "varlen_" + c["name"], "sequences": rv["nseq"],
+                "workload": name, "sequences": rv["nseq"],
                 "ms": round(rv["ms"], 4), "tflops": round(rv["tflops"], 2),
-                "roofline": {"bound": "mfma", "achieved": round(rv["tflops"], 2),
-                             "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                             "frac": round(rv["tflops"] / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
-                             "kernels": "k_mask_tiles + k_mask_order + k_attn_fwd_d128 (one "
-                                        "attn_fwd_varlen call, timed together)"},
+                "roofline": mfma_roofline(rv["tflops"], MFMA_BF16_PEAK_TFLOPS, name,
+                                          kernels="k_mask_tiles + k_mask_order + k_attn_fwd_d128 "
+                                                  "(one attn_fwd_varlen call, timed together)"),
             }
-            results[varlen_res["workload"]] = {"ms": varlen_res["ms"], "tflops": varlen_res["tflops"]}
+            results[name] = {"ms": varlen_res["ms"], "tflops": varlen_res["tflops"]}
             print(f"[bench] config 7 (config 4 packed, varlen): {rv['ms']:.3f} ms, "
                   f"{rv['tflops']:.1f} TFLOP/s", file=sys.stderr, flush=True)
         if cid == 2 and 8 in cfg_ids:
             # the same workload with the ALiBi distance bias (geometric slopes)
-            import torch as _t
-            slopes = _t.tensor([2.0 ** (-8.0 * (h + 1) / c["Hq"]) for h in range(c["Hq"])],
-                               dtype=_t.float32, device=dev)
+            slopes = torch.tensor([2.0 ** (-8.0 * (h + 1) / c["Hq"]) for h in range(c["Hq"])],
+                                  dtype=torch.float32, device=dev)
             wa = dict(w, kw_dev=dict(w["kw_dev"], alibi_slopes=slopes))
             ra = bench_fwd(ea, wa, args.steps, args.warmup)
+            name = "alibi_" + c["name"]
             alibi_res = {
-                "workload": "alibi_" + c["name"], "slopes": "2^(-8(h+1)/H)",
+                "workload": name, "slopes": "2^(-8(h+1)/H)",
                 "ms_step": round(ra["ms_step"], 4), "ms_kernel": round(ra["ms_kernel"], 4),
                 "tflops_kernel": round(ra["tflops_kernel"], 2),
-                "roofline": {"bound": "mfma", "achieved": round(ra["tflops_kernel"], 2),
-                             "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                             "frac": round(ra["tflops_kernel"] / MFMA_BF16_PEAK_TFLOPS, 4),
-                             "traffic": None, "kernel": "k_attn_fwd_d128_alibi"},
+                "roofline": mfma_roofline(ra["tflops_kernel"], MFMA_BF16_PEAK_TFLOPS, name,
+                                          kernel="k_attn_fwd_d128_alibi"),
             }
-            results[alibi_res["workload"]] = {"ms_kernel": alibi_res["ms_kernel"],
-                                              "tflops_kernel": alibi_res["tflops_kernel"]}
+            results[name] = {"ms_kernel": alibi_res["ms_kernel"],
+                             "tflops_kernel": alibi_res["tflops_kernel"]}
             print(f"[bench] config 8 (config 2 with ALiBi): {ra['ms_kernel']:.3f} ms kernel, "
                   f"{ra['tflops_kernel']:.1f} TFLOP/s", file=sys.stderr, flush=True)
         if cid == 2 and 9 in cfg_ids:
             rf = bench_fp8(ea, dict(w, cfg=gen.CONFIGS[9]), args.steps, args.warmup)
+            name = gen.CONFIGS[9]["name"]
             fp8_res = {
-                "workload": gen.CONFIGS[9]["name"],
+                "workload": name,
                 "rotation": "diag(random signs) * Hadamard / sqrt(128) on Q and K",
                 "ms_kernel": round(rf["ms_kernel"], 4),
                 "kernel_median_ms": round(rf["dist"]["median_ms"], 4),
                 "tflops_kernel": round(rf["tflops_kernel"], 2),
                 "ms_quantize_qkv": round(rf["ms_quant"], 4),
                 "quantize_gbs": round(rf["quant_gbs"], 1),
-                "roofline": {"bound": "mfma", "achieved": round(rf["tflops_kernel"], 2),
-                             "peak": MFMA_FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
-                             "frac": round(rf["tflops_kernel"] / MFMA_FP8_PEAK_TFLOPS, 4),
-                             "traffic": measured_traffic("k_attn_fwd8_d128"),
-                             "kernel": "k_attn_fwd8_d128"},
+                "roofline": mfma_roofline(rf["tflops_kernel"], MFMA_FP8_PEAK_TFLOPS, name,
+                                          kernel="k_attn_fwd8_d128"),
             }
-            results[fp8_res["workload"]] = {"ms_kernel": fp8_res["ms_kernel"],
-                                            "tflops_kernel": fp8_res["tflops_kernel"]}
+            results[name] = {"ms_kernel": fp8_res["ms_kernel"],
+                             "tflops_kernel": fp8_res["tflops_kernel"]}
             print(f"[bench] config 9 (config 2 in FP8): {rf['ms_kernel']:.3f} ms kernel, "
                   f"{rf['tflops_kernel']:.1f} TFLOP/s; quantize {rf['ms_quant']:.3f} ms",
                   file=sys.stderr, flush=True)
-        if cid == 2:
+        if cid == 2 and r is not None:
             headline = (w, r)
         else:
             del w
@@ -566,7 +610,7 @@ def main(argv=None):
             "algorithmic_bytes": wd["bytes"], "gbs": round(r["gbs"], 1),
             "roofline": {"bound": "hbm", "achieved": round(r["gbs"], 1), "peak": HBM_PEAK_GBS,
                          "unit": "GB/s", "frac": round(r["gbs"] / HBM_PEAK_GBS, 4),
-                         "traffic": measured_traffic("k_decode_split"),
+                         "traffic": measured_traffic(c["name"]),
                          "kernels": "k_decode_split + k_decode_combine (timed together)"},
         }
         results[c["name"]] = {"ms": decode_res["ms"], "gbs": decode_res["gbs"],
@@ -590,7 +634,7 @@ def main(argv=None):
             "flops": flops, "tflops": round(tf, 2),
             "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
-                         "traffic": measured_traffic("attn_bwd_d128"),
+                         "traffic": measured_traffic(c["name"]),
                          "kernels": "k_bwd_mask_kv + k_bwd_prep + k_bwd_dq + k_bwd_dkdv and the "
                                     "forward block mask (one attn_bwd call, timed together)"},
         }
@@ -613,12 +657,8 @@ def main(argv=None):
                        "N": c["N"], "d": c["d"], "mask": "causal", "scale": w["scale"],
                        "flops_per_step": w["flops"],
                        "step": "attn_fwd building its block mask, then the forward kernel"},
-            "roofline": {"bound": "mfma", "achieved": round(r["tflops_kernel"], 2),
-                         "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                         "frac": round(r["tflops_kernel"] / MFMA_BF16_PEAK_TFLOPS, 4),
-                         "traffic": measured_traffic("k_attn_fwd_d128"),
-                         "kernel": "k_attn_fwd_d128",
-                         "kernel_ms": round(r["ms_kernel"], 4)},
+            "roofline": mfma_roofline(r["tflops_kernel"], MFMA_BF16_PEAK_TFLOPS, c["name"],
+                                      kernel="k_attn_fwd_d128", kernel_ms=round(r["ms_kernel"], 4)),
         })
         if not args.no_cpu_baseline:
             print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
