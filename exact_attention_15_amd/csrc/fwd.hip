@@ -278,38 +278,32 @@ __device__ __forceinline__ void attn_fwd_body(const FwdParams &p) {
                 }
             }
         }
-        if constexpr (SOFTCAP) {
-            // Without the bias, a tile whose raw scores all lie in
-            // |scale * s / c| <= 0.15 (a wave-uniform test) takes the
-            // polynomial form of the cap: four VALU operations per score
-            // instead of an exponential, a reciprocal and three more.
-            bool poly = false;
-            if constexpr (!ALIBI) {
-                float am[4];
+        // Without the bias, a tile whose raw scores all lie in
+        // |scale * s / c| <= 0.15 (a wave-uniform test) takes the polynomial
+        // form of the cap instead of an exponential and a reciprocal.
+        // Without the bias the cap is also fused into the exponent (CAPFUSE):
+        // the row max is taken on the raw scores and capped once (the cap is
+        // increasing), and each score's capped value minus the reference max
+        // is a single FMA.
+        constexpr bool CAPFUSE = SOFTCAP && !ALIBI;
+        bool poly = false;
+        if constexpr (CAPFUSE) {
+            float am[4];
 #pragma unroll
-                for (int k = 0; k < 4; ++k) am[k] = fmaxf(fabsf(t[k]), fabsf(t[k + 4]));
+            for (int k = 0; k < 4; ++k) am[k] = fmaxf(fabsf(t[k]), fabsf(t[k + 4]));
 #pragma unroll
-                for (int i = 8; i < 32; i += 4)
+            for (int i = 8; i < 32; i += 4)
 #pragma unroll
-                    for (int k = 0; k < 4; ++k) am[k] = fmaxf(am[k], fabsf(t[i + k]));
-                const float a = fmaxf(fmaxf(am[0], am[1]), fmaxf(am[2], am[3]));
-                poly = __all(a <= p.cap_poly_lim);
-            }
-            if (poly) {
+                for (int k = 0; k < 4; ++k) am[k] = fmaxf(am[k], fabsf(t[i + k]));
+            const float a = fmaxf(fmaxf(am[0], am[1]), fmaxf(am[2], am[3]));
+            poly = __all(a <= p.cap_poly_lim);
+        }
+        if constexpr (SOFTCAP && ALIBI) {
+            // with the bias the score is already scaled (base-2 units)
 #pragma unroll
-                for (int j = 0; j < 32; ++j) {
-                    const float r2 = t[j] * t[j];
-                    const float q = __builtin_fmaf(__builtin_fmaf(p.cap_poly[2], r2, p.cap_poly[1]), r2, p.cap_poly[0]);
-                    t[j] *= q;
-                }
-            } else {
-                // with the bias the score is already scaled (base-2 units)
-                const float k2 = ALIBI ? p.cap_inv2 : p.cap_inv_scale_2log2e;
-#pragma unroll
-                for (int j = 0; j < 32; ++j) {
-                    const float e = __builtin_amdgcn_exp2f(t[j] * k2);
-                    t[j] = p.cap_log2 - p.cap_log2_2 * __builtin_amdgcn_rcpf(e + 1.f);
-                }
+            for (int j = 0; j < 32; ++j) {
+                const float e = __builtin_amdgcn_exp2f(t[j] * p.cap_inv2);
+                t[j] = p.cap_log2 - p.cap_log2_2 * __builtin_amdgcn_rcpf(e + 1.f);
             }
         }
         if (partial) {
@@ -333,6 +327,17 @@ __device__ __forceinline__ void attn_fwd_body(const FwdParams &p) {
         float mt = fmaxf(fmaxf(mx[0], mx[1]), fmaxf(mx[2], mx[3]));
         mt = fmaxf(mt, wave_swap_halves(mt, half));
         if constexpr (!SCALED) mt *= p.scale_log2;
+        if constexpr (CAPFUSE) {
+            // the cap of the raw row max (-inf stays -inf in the polynomial
+            // form: its highest coefficient is positive)
+            if (poly) {
+                const float r2 = mt * mt;
+                mt *= __builtin_fmaf(__builtin_fmaf(p.cap_poly[2], r2, p.cap_poly[1]), r2, p.cap_poly[0]);
+            } else if (mt != -INFINITY) {
+                const float e = __builtin_amdgcn_exp2f(mt * p.cap_inv_scale_2log2e);
+                mt = p.cap_log2 - p.cap_log2_2 * __builtin_amdgcn_rcpf(e + 1.f);
+            }
+        }
         // Rescale O and l only when some valid row's max grew by more than
         // RESCALE_LOG2 (a wave-uniform decision); otherwise keep the older,
         // smaller reference max: p stays <= 2^RESCALE_LOG2 and the result is
@@ -349,13 +354,39 @@ __device__ __forceinline__ void attn_fwd_body(const FwdParams &p) {
         }
         const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
         float ps[4] = {0.f, 0.f, 0.f, 0.f};
+        if constexpr (CAPFUSE) {
+            if (poly) {
+                // s (a0 + s^2 (a1 + s^2 a2)) - m as one FMA; a masked score
+                // (-inf) gives -inf * +inf - m = -inf
 #pragma unroll
-        for (int j = 0; j < 32; ++j) {
-            if constexpr (SCALED)
-                t[j] = __builtin_amdgcn_exp2f(t[j] - m_use);
-            else
-                t[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(t[j], p.scale_log2, -m_use));
-            ps[j & 3] += t[j];
+                for (int j = 0; j < 32; ++j) {
+                    const float r2 = t[j] * t[j];
+                    const float q = __builtin_fmaf(__builtin_fmaf(p.cap_poly[2], r2, p.cap_poly[1]), r2, p.cap_poly[0]);
+                    t[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(t[j], q, -m_use));
+                    ps[j & 3] += t[j];
+                }
+            } else {
+                // c log2e - 2 c log2e / (exp(2 scale s / c) + 1) - m, with
+                // the masked scores (finite here) put back to -inf
+                const float cm = p.cap_log2 - m_use;
+#pragma unroll
+                for (int j = 0; j < 32; ++j) {
+                    const float e = __builtin_amdgcn_exp2f(t[j] * p.cap_inv_scale_2log2e);
+                    float x = __builtin_fmaf(-p.cap_log2_2, __builtin_amdgcn_rcpf(e + 1.f), cm);
+                    if (partial && t[j] == -INFINITY) x = -INFINITY;
+                    t[j] = __builtin_amdgcn_exp2f(x);
+                    ps[j & 3] += t[j];
+                }
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < 32; ++j) {
+                if constexpr (SCALED)
+                    t[j] = __builtin_amdgcn_exp2f(t[j] - m_use);
+                else
+                    t[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(t[j], p.scale_log2, -m_use));
+                ps[j & 3] += t[j];
+            }
         }
         // one explicit FMA (alpha = 1 without a rescale), so that the sum
         // rounds the same way in both unrolled copies of the step whatever
