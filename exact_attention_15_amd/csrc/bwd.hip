@@ -356,6 +356,11 @@ __device__ __forceinline__ void bwd_dq_body(const BwdParams &p) {
         lse2 = p.lse2[r];
         dd = p.dvec[r];
     }
+    // Element mask of PARTIAL tiles, as in the forward: key is visible iff
+    // key - lo <= hi - lo as unsigned numbers; a row with no visible key
+    // gets an offset that puts every key outside (keys stay below 2^30).
+    const uint32_t vis_w = hi >= lo ? uint32_t(hi - lo) : 0u;
+    const uint32_t vis_pad = hi >= lo ? 0u : 0x40000000u;
 
     const int ntiles = __builtin_amdgcn_readfirstlane(p.mask.count[item]);
     const int32_t *tiles = p.mask.list + int64_t(item) * p.nkt;
@@ -407,11 +412,16 @@ __device__ __forceinline__ void bwd_dq_body(const BwdParams &p) {
                 } else {
                     pj = __builtin_amdgcn_exp2f(__builtin_fmaf(s, p.scale_log2, -lse2));
                 }
-                if (partial) {
-                    const int key = kt * BLOCK_N + 32 * (j >> 4) + acc_row(j & 15, half);
-                    if (key < lo || key > hi) pj = 0.f;
-                }
                 ds[j] = pj * fac;
+            }
+            // The mask is a loop of its own under one branch: tested inside
+            // the loop above, the compiler turned it into selects that ran
+            // on every tile.
+            if (partial) {
+                const uint32_t nl = uint32_t(kt * BLOCK_N + 4 * half - lo) + vis_pad;
+#pragma unroll
+                for (int j = 0; j < 32; ++j)
+                    if (uint32_t(32 * (j >> 4) + acc_row(j & 15, 0)) + nl > vis_w) ds[j] = 0.f;
             }
         }
         {
