@@ -127,6 +127,12 @@ __device__ __forceinline__ void attn_fwd_body(const FwdParams &p) {
 
     const int ntiles = __builtin_amdgcn_readfirstlane(p.mask.count[item]);
     const int32_t *tiles = p.mask.list + int64_t(item) * p.nkt;
+    // With the distance bias the key tiles are visited from the last listed
+    // (nearest the diagonal under a causal mask, where the bias is smallest)
+    // down, so that a row's max is met early and later tiles rarely raise
+    // it: in ascending order a steep slope raised it at every tile and each
+    // raise rescaled the accumulator.
+    auto tile_at = [&](int i) { return ALIBI ? tiles[ntiles - 1 - i] : tiles[i]; };
     const uint16_t *kbase = p.k + b * p.k_sb + hk * p.k_sh;
     const uint16_t *vbase = p.v + b * p.v_sb + hk * p.v_sh;
 
@@ -211,7 +217,7 @@ __device__ __forceinline__ void attn_fwd_body(const FwdParams &p) {
         const int kt = ent >> 1;
         const bool partial = ent & TILE_PARTIAL;
         const int ent_next = __builtin_amdgcn_readfirstlane(ent_next_v);
-        const int ent_next2_v = tiles[min(it + 2, ntiles - 1)];
+        const int ent_next2_v = tile_at(min(it + 2, ntiles - 1));
         // The other buffer was last read in iteration it-1, which every wave
         // has finished (barrier at the end of it), so it can be refilled now.
         if (it + 1 < ntiles) issue_tile(ent_next >> 1, 1 - stage);
@@ -443,9 +449,9 @@ __device__ __forceinline__ void attn_fwd_body(const FwdParams &p) {
     };
 
     if (ntiles > 0) {
-        ent_cur = __builtin_amdgcn_readfirstlane(tiles[0]);
+        ent_cur = __builtin_amdgcn_readfirstlane(tile_at(0));
         issue_tile(ent_cur >> 1, 0);
-        ent_next_v = tiles[min(1, ntiles - 1)];
+        ent_next_v = tile_at(min(1, ntiles - 1));
     }
     wait_vmem_all();
     __syncthreads();
