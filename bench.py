@@ -79,50 +79,50 @@ MEASURED_TRAFFIC = {
     "causal_b8_h32_n4096_d128": (
         "k_attn_fwd_d128",
         ["fwd.hip", "tile.h", "common.h", "../build.py"],
-        "7c27c81005dd02fbb2328209dc0787ada9f819f8056620fb11d9e037971f5ca8",
-        1117978228,
+        "1ad46c73441d4b070cb1ce11757a3e2bfaf65be08087066387187da5044aed76",
+        1117231184,
         "profiles/k_attn_fwd_d128_causal_b8_h32_n4096_d128.md"),
     "window1024_softcap50_b4_h32_n16384_d128": (
         "k_attn_fwd_d128_softcap",
         ["fwd.hip", "tile.h", "common.h", "../build.py"],
-        "7c27c81005dd02fbb2328209dc0787ada9f819f8056620fb11d9e037971f5ca8",
-        2498594933,
+        "1ad46c73441d4b070cb1ce11757a3e2bfaf65be08087066387187da5044aed76",
+        2463612860,
         "profiles/k_attn_fwd_d128_softcap_window1024_softcap50_b4_h32_n16384_d128.md"),
     "gqa32x8_docs_causal_b2_n8192_d128": (
         "k_attn_fwd_d128",
         ["fwd.hip", "tile.h", "common.h", "../build.py"],
-        "7c27c81005dd02fbb2328209dc0787ada9f819f8056620fb11d9e037971f5ca8",
-        399013389,
+        "1ad46c73441d4b070cb1ce11757a3e2bfaf65be08087066387187da5044aed76",
+        399072217,
         "profiles/k_attn_fwd_d128_gqa32x8_docs_causal_b2_n8192_d128.md"),
     "varlen_gqa32x8_docs_causal_b2_n8192_d128": (
         "k_mask_tiles + k_mask_order + k_attn_fwd_d128",
         ["fwd.hip", "tile.h", "common.h", "../build.py", "mask.hip"],
-        "85e0cd12bee21745fba15a5185d99a3081469cc4de417a0dd176425bceb9bbb3",
-        607866621,
+        "151c2ec3c08e77902cb60eb9811840b3eb2ee2285028ba0e72bb96faccda7b54",
+        608143887,
         "profiles/attn_fwd_varlen_gqa32x8_docs_b2_n8192_d128.md"),
     "alibi_causal_b8_h32_n4096_d128": (
         "k_attn_fwd_d128_alibi",
         ["fwd.hip", "tile.h", "common.h", "../build.py"],
-        "7c27c81005dd02fbb2328209dc0787ada9f819f8056620fb11d9e037971f5ca8",
-        1116309633,
+        "1ad46c73441d4b070cb1ce11757a3e2bfaf65be08087066387187da5044aed76",
+        1192375621,
         "profiles/k_attn_fwd_d128_alibi_causal_b8_h32_n4096_d128.md"),
     "fp8_causal_b8_h32_n4096_d128": (
         "k_attn_fwd8_d128",
         ["fwd8.hip", "tile.h", "common.h", "../build.py"],
-        "ab3c5295ee176b12ec79b86e39f5e07cffab2d8ba234a0c4e8e1727156858793",
-        679392187,
+        "2a0a81eb691acfce4ebc5c2a5145541e608f76b8a66157b914f202e244cea4fc",
+        687511582,
         "profiles/k_attn_fwd8_d128_causal_b8_h32_n4096_d128.md"),
     "decode_b16_gqa32x8_t32768_d128_chunk1024": (
         "k_decode_split + k_decode_combine",
         ["decode.hip", "common.h", "../build.py"],
         "c3772f0195e9a3d4a50501737135247e92e96facd1467ab377dc3f2ee413cb07",
-        961770538,
+        961752569,
         "profiles/k_decode_split_decode_b16_gqa32x8_t32768_d128.md"),
     "bwd_causal_b8_h32_n4096_d128": (
         "all kernels of one attn_bwd call",
         ["bwd.hip", "tile.h", "common.h", "mask.hip", "../build.py"],
-        "d19dd1e65f641f7a39c1039019b9e98b7d7a6f6dd30caa6c903bf18106bc2596",
-        3610043247,
+        "edd5c189ef27531d6627cd593251cb0231d135520d76e7cdb80e42fa122b31a8",
+        3551773092,
         "profiles/k_bwd_d128_causal_b8_h32_n4096_d128.md"),
 }
 

@@ -1,6 +1,7 @@
 // Issue rates on gfx950 with register operands only: VALU FMA, v_exp_f32,
 // v_mfma_f32_32x32x16_bf16, MFMA and VALU in one wave, and MFMA in one wave
-// beside VALU in the other wave of the same SIMD.  One 4- or 8-wave
+// beside VALU in the other wave of the same SIMD, and chains of dependent
+// MFMAs (the accumulator of each the input of the next).  One 4- or 8-wave
 // workgroup per CU (96 KiB of LDS each), so each SIMD holds 1 or 2 of them;
 // in an 8-wave workgroup waves w and w+4 share a SIMD (the map is printed
 // first).  Times are s_memtime ticks per loop iteration per wave, and the
@@ -38,8 +39,18 @@ __device__ __forceinline__ void mfma8(f32x16 (&c)[4], bf16x8 a, bf16x8 b) {
         for (int i = 0; i < 4; ++i) c[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c[i], 0, 0, 0);
 }
 
+// 8 MFMAs on NACC accumulators taken in turn: each MFMA depends on the one
+// NACC places before it (NACC = 1: one chain of dependent MFMAs).
+template <int NACC> __device__ __forceinline__ void mfma8_chains(f32x16 (&c)[4], bf16x8 a, bf16x8 b) {
+#pragma unroll
+    for (int r = 0; r < 8 / NACC; ++r)
+#pragma unroll
+        for (int i = 0; i < NACC; ++i) c[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c[i], 0, 0, 0);
+}
+
 // MODE 0: 32 FMA; 1: 16 exp; 2: 8 MFMA; 3: waves 0-3 8 MFMA, 4-7 32 FMA;
-// 4: waves 0-3 8 MFMA, 4-7 16 exp; 5: 8 MFMA and 32 FMA in every wave
+// 4: waves 0-3 8 MFMA, 4-7 16 exp; 5: 8 MFMA and 32 FMA in every wave;
+// 6: 8 MFMA in one dependent chain; 7: 8 MFMA in two chains taken in turn
 template <int MODE>
 __global__ __launch_bounds__(512) void k_units(float x, long long *ticks, float *sink) {
     __shared__ float pad[24 * 1024]; // 96 KiB: one workgroup per CU
@@ -64,7 +75,9 @@ __global__ __launch_bounds__(512) void k_units(float x, long long *ticks, float 
         else if constexpr (MODE == 2) { mfma8(c, av, bv); }
         else if constexpr (MODE == 3) { if (w < 4) mfma8(c, av, bv); else { fma16(a, x); fma16(a, x); } }
         else if constexpr (MODE == 4) { if (w < 4) mfma8(c, av, bv); else exp16(a); }
-        else { mfma8(c, av, bv); fma16(a, x); fma16(a, x); }
+        else if constexpr (MODE == 5) { mfma8(c, av, bv); fma16(a, x); fma16(a, x); }
+        else if constexpr (MODE == 6) { mfma8_chains<1>(c, av, bv); }
+        else { mfma8_chains<2>(c, av, bv); }
     }
     const long long t1 = __builtin_amdgcn_s_memtime();
     float s = 0.f;
@@ -108,14 +121,16 @@ int main() {
     CHECK(hipMalloc(&ticks, nb * 8 * sizeof(long long)));
     CHECK(hipMalloc(&sink, 512 * sizeof(float)));
     const char *names[] = {"32 FMA", "16 v_exp_f32", "8 MFMA 32x32x16 bf16", "8 MFMA (waves 0-3) | 32 FMA (waves 4-7)",
-                           "8 MFMA (waves 0-3) | 16 exp (waves 4-7)", "8 MFMA + 32 FMA in every wave"};
-    void (*kern[6])(float, long long *, float *) = {k_units<0>, k_units<1>, k_units<2>, k_units<3>, k_units<4>, k_units<5>};
+                           "8 MFMA (waves 0-3) | 16 exp (waves 4-7)", "8 MFMA + 32 FMA in every wave",
+                           "8 MFMA, one dependent chain", "8 MFMA, two chains in turn"};
+    void (*kern[8])(float, long long *, float *) = {k_units<0>, k_units<1>, k_units<2>, k_units<3>,
+                                                     k_units<4>, k_units<5>, k_units<6>, k_units<7>};
     hipEvent_t e0, e1;
     CHECK(hipEventCreate(&e0));
     CHECK(hipEventCreate(&e1));
     printf("%-8s %-44s %14s %14s %10s\n", "waves/WG", "per loop iteration", "ticks w0-3", "ticks w4-7", "tick GHz");
     for (int waves : {4, 8}) {
-        for (int mode = 0; mode < 6; ++mode) {
+        for (int mode = 0; mode < 8; ++mode) {
             if (waves == 4 && (mode == 3 || mode == 4)) continue;
             hipLaunchKernelGGL(kern[mode], dim3(nb), dim3(64 * waves), 0, 0, 1.0001f, ticks, sink);
             CHECK(hipDeviceSynchronize());
