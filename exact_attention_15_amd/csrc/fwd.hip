@@ -322,78 +322,103 @@ __device__ __forceinline__ void attn_fwd_body(const FwdParams &p) {
         }
 
         // ---- online softmax ----
-        // Row max and sum as 4-way trees: short dependency chains.
-        float mx[4];
+        // The exponentials are formed first against the current reference
+        // max.  If every lane's 32 probabilities sum below 2^RESCALE_LOG2,
+        // none of them reaches it, so no row's max has risen past the
+        // reference by RESCALE_LOG2 and nothing is rescaled: the row-max
+        // tree is skipped.  Otherwise (and while some row has no reference
+        // yet) the max is taken and the rescale decided as before, and the
+        // exponentials are formed again if the reference moved.  The result
+        // is the same either way.
+        auto exps = [&](float m_use, float (&pv)[32], float (&ps)[4]) {
 #pragma unroll
-        for (int k = 0; k < 4; ++k) mx[k] = fmaxf(t[k], t[k + 4]);
+            for (int k = 0; k < 4; ++k) ps[k] = 0.f;
+            if constexpr (CAPFUSE) {
+                if (poly) {
+                    // s (a0 + s^2 (a1 + s^2 a2)) - m as one FMA; a masked
+                    // score (-inf) gives -inf * +inf - m = -inf
 #pragma unroll
-        for (int i = 8; i < 32; i += 4)
+                    for (int j = 0; j < 32; ++j) {
+                        const float r2 = t[j] * t[j];
+                        const float q = __builtin_fmaf(__builtin_fmaf(p.cap_poly[2], r2, p.cap_poly[1]), r2, p.cap_poly[0]);
+                        pv[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(t[j], q, -m_use));
+                        ps[j & 3] += pv[j];
+                    }
+                } else {
+                    // c log2e - 2 c log2e / (exp(2 scale s / c) + 1) - m, with
+                    // the masked scores (finite here) put back to -inf
+                    const float cm = p.cap_log2 - m_use;
 #pragma unroll
-            for (int k = 0; k < 4; ++k) mx[k] = fmaxf(mx[k], t[i + k]);
-        float mt = fmaxf(fmaxf(mx[0], mx[1]), fmaxf(mx[2], mx[3]));
-        mt = fmaxf(mt, wave_swap_halves(mt, half));
-        if constexpr (!SCALED) mt *= p.scale_log2;
-        if constexpr (CAPFUSE) {
-            // the cap of the raw row max (-inf stays -inf in the polynomial
-            // form: its highest coefficient is positive)
-            if (poly) {
-                const float r2 = mt * mt;
-                mt *= __builtin_fmaf(__builtin_fmaf(p.cap_poly[2], r2, p.cap_poly[1]), r2, p.cap_poly[0]);
-            } else if (mt != -INFINITY) {
-                const float e = __builtin_amdgcn_exp2f(mt * p.cap_inv_scale_2log2e);
-                mt = p.cap_log2 - p.cap_log2_2 * __builtin_amdgcn_rcpf(e + 1.f);
-            }
-        }
-        // Rescale O and l only when some valid row's max grew by more than
-        // RESCALE_LOG2 (a wave-uniform decision); otherwise keep the older,
-        // smaller reference max: p stays <= 2^RESCALE_LOG2 and the result is
-        // exact, since O, l and the LSE all use the same reference.  Rows
-        // past N never vote, so the decision does not depend on whether
-        // fully visible tiles are element-masked.
-        const float m_new = fmaxf(m_run, mt);
-        float alpha = 1.f;
-        if (__any(row_ok && m_new > m_run + RESCALE_LOG2)) {
-            alpha = __builtin_amdgcn_exp2f(m_run - (m_new == -INFINITY ? 0.f : m_new));
-#pragma unroll
-            for (int i = 0; i < C::DBLK; ++i) acc_o[i] *= alpha;
-            m_run = m_new;
-        }
-        const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
-        float ps[4] = {0.f, 0.f, 0.f, 0.f};
-        if constexpr (CAPFUSE) {
-            if (poly) {
-                // s (a0 + s^2 (a1 + s^2 a2)) - m as one FMA; a masked score
-                // (-inf) gives -inf * +inf - m = -inf
-#pragma unroll
-                for (int j = 0; j < 32; ++j) {
-                    const float r2 = t[j] * t[j];
-                    const float q = __builtin_fmaf(__builtin_fmaf(p.cap_poly[2], r2, p.cap_poly[1]), r2, p.cap_poly[0]);
-                    t[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(t[j], q, -m_use));
-                    ps[j & 3] += t[j];
+                    for (int j = 0; j < 32; ++j) {
+                        const float e = __builtin_amdgcn_exp2f(t[j] * p.cap_inv_scale_2log2e);
+                        float x = __builtin_fmaf(-p.cap_log2_2, __builtin_amdgcn_rcpf(e + 1.f), cm);
+                        if (partial && t[j] == -INFINITY) x = -INFINITY;
+                        pv[j] = __builtin_amdgcn_exp2f(x);
+                        ps[j & 3] += pv[j];
+                    }
                 }
             } else {
-                // c log2e - 2 c log2e / (exp(2 scale s / c) + 1) - m, with
-                // the masked scores (finite here) put back to -inf
-                const float cm = p.cap_log2 - m_use;
 #pragma unroll
                 for (int j = 0; j < 32; ++j) {
-                    const float e = __builtin_amdgcn_exp2f(t[j] * p.cap_inv_scale_2log2e);
-                    float x = __builtin_fmaf(-p.cap_log2_2, __builtin_amdgcn_rcpf(e + 1.f), cm);
-                    if (partial && t[j] == -INFINITY) x = -INFINITY;
-                    t[j] = __builtin_amdgcn_exp2f(x);
-                    ps[j & 3] += t[j];
+                    if constexpr (SCALED)
+                        pv[j] = __builtin_amdgcn_exp2f(t[j] - m_use);
+                    else
+                        pv[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(t[j], p.scale_log2, -m_use));
+                    ps[j & 3] += pv[j];
                 }
             }
-        } else {
-#pragma unroll
-            for (int j = 0; j < 32; ++j) {
-                if constexpr (SCALED)
-                    t[j] = __builtin_amdgcn_exp2f(t[j] - m_use);
-                else
-                    t[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(t[j], p.scale_log2, -m_use));
-                ps[j & 3] += t[j];
-            }
+        };
+        float pv[32], ps[4];
+        float alpha = 1.f;
+        const bool fresh = __any(row_ok && m_run == -INFINITY);
+        bool need_max = fresh;
+        if (!fresh) {
+            exps(m_run, pv, ps);
+            const float lsum = (ps[0] + ps[1]) + (ps[2] + ps[3]);
+            need_max = __any(row_ok && !(lsum < float(1 << int(RESCALE_LOG2))));
         }
+        if (need_max) {
+            // Row max and sum as 4-way trees: short dependency chains.
+            float mx[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) mx[k] = fmaxf(t[k], t[k + 4]);
+#pragma unroll
+            for (int i = 8; i < 32; i += 4)
+#pragma unroll
+                for (int k = 0; k < 4; ++k) mx[k] = fmaxf(mx[k], t[i + k]);
+            float mt = fmaxf(fmaxf(mx[0], mx[1]), fmaxf(mx[2], mx[3]));
+            mt = fmaxf(mt, wave_swap_halves(mt, half));
+            if constexpr (!SCALED) mt *= p.scale_log2;
+            if constexpr (CAPFUSE) {
+                // the cap of the raw row max (-inf stays -inf in the polynomial
+                // form: its highest coefficient is positive)
+                if (poly) {
+                    const float r2 = mt * mt;
+                    mt *= __builtin_fmaf(__builtin_fmaf(p.cap_poly[2], r2, p.cap_poly[1]), r2, p.cap_poly[0]);
+                } else if (mt != -INFINITY) {
+                    const float e = __builtin_amdgcn_exp2f(mt * p.cap_inv_scale_2log2e);
+                    mt = p.cap_log2 - p.cap_log2_2 * __builtin_amdgcn_rcpf(e + 1.f);
+                }
+            }
+            // Rescale O and l only when some valid row's max grew by more than
+            // RESCALE_LOG2 (a wave-uniform decision); otherwise keep the older,
+            // smaller reference max: p stays <= 2^RESCALE_LOG2 and the result is
+            // exact, since O, l and the LSE all use the same reference.  Rows
+            // past N never vote, so the decision does not depend on whether
+            // fully visible tiles are element-masked.
+            const float m_new = fmaxf(m_run, mt);
+            bool moved = false;
+            if (__any(row_ok && m_new > m_run + RESCALE_LOG2)) {
+                alpha = __builtin_amdgcn_exp2f(m_run - (m_new == -INFINITY ? 0.f : m_new));
+#pragma unroll
+                for (int i = 0; i < C::DBLK; ++i) acc_o[i] *= alpha;
+                m_run = m_new;
+                moved = true;
+            }
+            if (fresh || moved) exps((m_run == -INFINITY) ? 0.f : m_run, pv, ps);
+        }
+#pragma unroll
+        for (int j = 0; j < 32; ++j) t[j] = pv[j];
         // one explicit FMA (alpha = 1 without a rescale), so that the sum
         // rounds the same way in both unrolled copies of the step whatever
         // the compiler contracts
