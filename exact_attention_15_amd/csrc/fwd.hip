@@ -230,6 +230,11 @@ __device__ __forceinline__ void attn_fwd_body(const FwdParams &p) {
         // use them, so LDS latency overlaps matrix work; the scheduling
         // groups pin that interleave (DS reads, then MFMAs, k-step by k-step).
         f32x16_t s0 = f32x16_t{}, s1 = f32x16_t{};
+        // The wave's priority is raised while it issues its MFMA blocks, so
+        // that a SIMD whose other wave is in its softmax issues the MFMAs
+        // first (+1% measured; raising it for the softmax instead gained
+        // nothing).
+        __builtin_amdgcn_s_setprio(1);
         {
             bf16x8_t ka[C::KSTEPS][2];
             auto kread = [&](int s) {
@@ -252,6 +257,7 @@ __device__ __forceinline__ void attn_fwd_body(const FwdParams &p) {
                 __builtin_amdgcn_sched_group_barrier(SCHED_MFMA, 2, 0);
             }
         }
+        __builtin_amdgcn_s_setprio(0);
 
         // ---- score_mod and mask in registers ----
         // Without a cap the raw dot products are kept and the scale is folded
@@ -437,6 +443,7 @@ __device__ __forceinline__ void attn_fwd_body(const FwdParams &p) {
         // k0 + {0..3} and k0 + 8 + {0..3}, k0 = 32kb + 16hh + 4*half, and the
         // V^T operand of those keys for d-block db; operands are read PV_AHEAD
         // MFMAs ahead.
+        __builtin_amdgcn_s_setprio(1);
         {
             constexpr int NM = 4 * C::DBLK;
             u32x4_t va[NM];
@@ -464,6 +471,7 @@ __device__ __forceinline__ void attn_fwd_body(const FwdParams &p) {
                 __builtin_amdgcn_sched_group_barrier(SCHED_MFMA, 1, 0);
             }
         }
+        __builtin_amdgcn_s_setprio(0);
 
         // The next tile's LDS writes must land before anyone reads them, and
         // this tile's buffer must be free before it is refilled.
