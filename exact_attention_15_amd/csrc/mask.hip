@@ -204,32 +204,48 @@ __global__ __launch_bounds__(256) void k_mask_tiles(attn_mask_spec spec, VarlenV
 // One workgroup per batch row: order[b][rank] = query tile, ranked by
 // descending visited-tile count (ties keep tile order), so the forward
 // kernel can hand out the heaviest query tiles of each batch row first.
-// The row's counts are staged in LDS when they fit (ORDER_LDS_TILES), so the
+// With documents or varlen sequences the tiles are first grouped by the
+// start of their first row's visible interval (its document), documents in
+// order: the workgroups that run at once then read one or two documents'
+// K/V, which stay in the XCD's L2, where heavy-first across all documents
+// ran the heaviest tiles of every document together (the packed GQA
+// document workload fetched 1.8x its compulsory bytes that way).
+// The row's keys are staged in LDS when they fit (ORDER_LDS_TILES), so the
 // rank loop reads LDS broadcasts instead of global memory.
-constexpr int ORDER_LDS_TILES = 16384;
-__global__ __launch_bounds__(1024) void k_mask_order(int nqt, const int32_t *count, int32_t *order) {
-    extern __shared__ int32_t s_cnt[];
+constexpr int ORDER_LDS_TILES = 8192;
+__global__ __launch_bounds__(1024) void k_mask_order(int nqt, int N, bool by_doc, const int32_t *count,
+                                                     const int32_t *lo, int32_t *order) {
+    extern __shared__ int32_t s_key[]; // [0, nqt): counts; [nqt, 2 nqt): document keys
     const int b = blockIdx.x;
     const int32_t *cb = count + int64_t(b) * nqt;
+    const int32_t *lb = lo + int64_t(b) * N;
     int32_t *ob = order + int64_t(b) * nqt;
     const bool in_lds = nqt <= ORDER_LDS_TILES;
+    auto doc_key = [&](int i) { return by_doc ? lb[int64_t(i) * BLOCK_M] : 0; };
     if (in_lds) {
-        for (int i = threadIdx.x; i < nqt; i += blockDim.x) s_cnt[i] = cb[i];
+        for (int i = threadIdx.x; i < nqt; i += blockDim.x) {
+            s_key[i] = cb[i];
+            s_key[nqt + i] = doc_key(i);
+        }
         __syncthreads();
     }
-    auto rank_all = [&](const auto *c) {
+    auto rank_all = [&](auto cnt_at, auto key_at) {
         for (int i = threadIdx.x; i < nqt; i += blockDim.x) {
-            const int ci = c[i];
+            const int ci = cnt_at(i), ki = key_at(i);
             int rank = 0;
             for (int j = 0; j < nqt; ++j) {
-                const int cj = c[j];
-                rank += (cj > ci) || (cj == ci && j < i);
+                const int cj = cnt_at(j), kj = key_at(j);
+                rank += (kj < ki) || (kj == ki && ((cj > ci) || (cj == ci && j < i)));
             }
             ob[rank] = i;
         }
     };
-    if (in_lds) rank_all((const __attribute__((address_space(3))) int32_t *)(s_cnt)); // generic -> LDS
-    else rank_all(cb);
+    if (in_lds) {
+        const __attribute__((address_space(3))) int32_t *sk = (const __attribute__((address_space(3))) int32_t *)(s_key);
+        rank_all([&](int i) { return sk[i]; }, [&](int i) { return sk[nqt + i]; });
+    } else {
+        rank_all([&](int i) { return cb[i]; }, doc_key);
+    }
 }
 
 hipError_t launch_mask_build(const attn_mask_spec &spec, const MaskLayout &L, void *out,
@@ -244,8 +260,10 @@ hipError_t launch_mask_build(const attn_mask_spec &spec, const MaskLayout &L, vo
                        lo, hi, cnt, list);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const size_t order_lds = L.nqt <= ORDER_LDS_TILES ? size_t(L.nqt) * sizeof(int32_t) : 0;
-    hipLaunchKernelGGL(k_mask_order, dim3(L.B), dim3(1024), order_lds, stream, L.nqt, cnt, order);
+    const size_t order_lds = L.nqt <= ORDER_LDS_TILES ? 2 * size_t(L.nqt) * sizeof(int32_t) : 0;
+    const bool by_doc = (spec.flags & ATTN_MASK_DOCS) || vl.cu_q != nullptr;
+    hipLaunchKernelGGL(k_mask_order, dim3(L.B), dim3(1024), order_lds, stream, L.nqt, L.N, by_doc, cnt, lo,
+                       order);
     return hipGetLastError();
 }
 

@@ -232,11 +232,13 @@ def test_mask_builder_matches_host(ea, kind, N):
             assert m["count"][b, qt].item() == len(expect)
             assert got == expect, (b, qt)
     # heavy-first order per batch row: a permutation, counts non-increasing,
-    # ties by tile index
+    # ties by tile index; with documents, grouped first by the interval start
+    # of each tile's first row (its document), documents in order
     order = m["order"].numpy().reshape(B, nqt)
     for b in range(B):
         assert sorted(order[b].tolist()) == list(range(nqt))
-        expect_order = sorted(range(nqt), key=lambda x: (-counts[b, x], x))
+        doc = (lambda x: int(lo[b, x * BM])) if kind == "docs" else (lambda x: 0)
+        expect_order = sorted(range(nqt), key=lambda x: (doc(x), -counts[b, x], x))
         assert order[b].tolist() == expect_order
 
 
