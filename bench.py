@@ -79,50 +79,50 @@ MEASURED_TRAFFIC = {
     "causal_b8_h32_n4096_d128": (
         "k_attn_fwd_d128",
         ["fwd.hip", "tile.h", "common.h", "../build.py"],
-        "1ad46c73441d4b070cb1ce11757a3e2bfaf65be08087066387187da5044aed76",
-        1117231184,
+        "0f81c7e8ff75e4a65c09cbb88236dc9e615987a9d7641cfa7af8da17b39feca1",
+        1098892425,
         "profiles/k_attn_fwd_d128_causal_b8_h32_n4096_d128.md"),
     "window1024_softcap50_b4_h32_n16384_d128": (
         "k_attn_fwd_d128_softcap",
         ["fwd.hip", "tile.h", "common.h", "../build.py"],
-        "1ad46c73441d4b070cb1ce11757a3e2bfaf65be08087066387187da5044aed76",
-        2463612860,
+        "0f81c7e8ff75e4a65c09cbb88236dc9e615987a9d7641cfa7af8da17b39feca1",
+        2444712249,
         "profiles/k_attn_fwd_d128_softcap_window1024_softcap50_b4_h32_n16384_d128.md"),
     "gqa32x8_docs_causal_b2_n8192_d128": (
         "k_attn_fwd_d128",
         ["fwd.hip", "tile.h", "common.h", "../build.py"],
-        "1ad46c73441d4b070cb1ce11757a3e2bfaf65be08087066387187da5044aed76",
-        399072217,
+        "0f81c7e8ff75e4a65c09cbb88236dc9e615987a9d7641cfa7af8da17b39feca1",
+        351172670,
         "profiles/k_attn_fwd_d128_gqa32x8_docs_causal_b2_n8192_d128.md"),
     "varlen_gqa32x8_docs_causal_b2_n8192_d128": (
         "k_mask_tiles + k_mask_order + k_attn_fwd_d128",
         ["fwd.hip", "tile.h", "common.h", "../build.py", "mask.hip"],
-        "151c2ec3c08e77902cb60eb9811840b3eb2ee2285028ba0e72bb96faccda7b54",
-        608143887,
+        "0f05cc1a2c778ce8ed424ee44c6f777002087d665d305bb06953c97a6865a915",
+        349434813,
         "profiles/attn_fwd_varlen_gqa32x8_docs_b2_n8192_d128.md"),
     "alibi_causal_b8_h32_n4096_d128": (
         "k_attn_fwd_d128_alibi",
         ["fwd.hip", "tile.h", "common.h", "../build.py"],
-        "1ad46c73441d4b070cb1ce11757a3e2bfaf65be08087066387187da5044aed76",
-        1192375621,
+        "0f81c7e8ff75e4a65c09cbb88236dc9e615987a9d7641cfa7af8da17b39feca1",
+        1161138002,
         "profiles/k_attn_fwd_d128_alibi_causal_b8_h32_n4096_d128.md"),
     "fp8_causal_b8_h32_n4096_d128": (
         "k_attn_fwd8_d128",
         ["fwd8.hip", "tile.h", "common.h", "../build.py"],
         "2a0a81eb691acfce4ebc5c2a5145541e608f76b8a66157b914f202e244cea4fc",
-        687511582,
+        686732329,
         "profiles/k_attn_fwd8_d128_causal_b8_h32_n4096_d128.md"),
     "decode_b16_gqa32x8_t32768_d128_chunk1024": (
         "k_decode_split + k_decode_combine",
         ["decode.hip", "common.h", "../build.py"],
         "c3772f0195e9a3d4a50501737135247e92e96facd1467ab377dc3f2ee413cb07",
-        961752569,
+        961753627,
         "profiles/k_decode_split_decode_b16_gqa32x8_t32768_d128.md"),
     "bwd_causal_b8_h32_n4096_d128": (
         "all kernels of one attn_bwd call",
         ["bwd.hip", "tile.h", "common.h", "mask.hip", "../build.py"],
-        "edd5c189ef27531d6627cd593251cb0231d135520d76e7cdb80e42fa122b31a8",
-        3551773092,
+        "0372b059131c2d151ce11750ac4511613fe6e6b80b251e13499ac246855f7e82",
+        3550863801,
         "profiles/k_bwd_d128_causal_b8_h32_n4096_d128.md"),
 }
 
