@@ -121,8 +121,8 @@ MEASURED_TRAFFIC = {
     "bwd_causal_b8_h32_n4096_d128": (
         "all kernels of one attn_bwd call",
         ["bwd.hip", "tile.h", "common.h", "mask.hip", "../build.py"],
-        "0372b059131c2d151ce11750ac4511613fe6e6b80b251e13499ac246855f7e82",
-        3550863801,
+        "5a8c372ca2a1d4ba486f6354e9a33390f46c0b4bef9fb7078b2d78645e22fd6d",
+        3284686419,
         "profiles/k_bwd_d128_causal_b8_h32_n4096_d128.md"),
 }
 
@@ -362,7 +362,7 @@ def bench_decode(ea, w, steps, warmup):
 
 
 def bench_bwd(ea, w, steps, warmup):
-    """attn_bwd (block masks, row prep, dQ kernel, dK/dV kernel) on the
+    """attn_bwd (block masks, dQ kernel with the per-row prep, dK/dV kernel) on the
     forward workload ``w`` with its own forward outputs and a seeded dO."""
     import torch
     c = w["cfg"]
@@ -635,7 +635,7 @@ def main(argv=None):
             "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
                          "traffic": measured_traffic(c["name"]),
-                         "kernels": "k_bwd_mask_kv + k_bwd_prep + k_bwd_dq + k_bwd_dkdv and the "
+                         "kernels": "k_bwd_mask_kv + k_bwd_dq + k_bwd_dkdv and the "
                                     "forward block mask (one attn_bwd call, timed together)"},
         }
         results[c["name"]] = {"ms": bwd_res["ms"], "tflops": bwd_res["tflops"],

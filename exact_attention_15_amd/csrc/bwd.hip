@@ -8,13 +8,14 @@
 // soft cap multiplies it by 1 - tanh^2 = 1 - (s' / c)^2; then
 // dQ = scale * dS K, dK = scale * dS^T Q and dV = P^T dO.
 //
-// Three kernels:
-//   k_bwd_prep   per row: D = dO . O and the base-2 LSE (+inf for a row with
-//                no visible key, so its recomputed P is 0);
+// Two gradient kernels, after the transposed block mask (k_bwd_mask_kv):
 //   k_bwd_dq     the forward's decomposition (128 query rows per workgroup,
-//                64-key tiles from the forward block mask): S^T = K Q^T and
-//                dP^T = V dO^T on the MFMA pipe, dS^T in registers, then
-//                dQ^T += K^T dS^T with K^T from LDS transpose reads;
+//                64-key tiles from the forward block mask): first, per row,
+//                D = dO . O and the base-2 LSE (+inf for a row with no
+//                visible key, so its recomputed P is 0), kept and written
+//                for the next kernel; then S^T = K Q^T and dP^T = V dO^T on
+//                the MFMA pipe, dS^T in registers, and dQ^T += K^T dS^T with
+//                K^T from LDS transpose reads;
 //   k_bwd_dkdv   128 keys per workgroup (K and V fragments held in registers,
 //                one key per lane column), streaming the 64-row Q and dO
 //                tiles of every query head of the GQA group: S = Q K^T,
@@ -109,49 +110,6 @@ __global__ __launch_bounds__(256) void k_bwd_mask_kv(int N, int nkb, int nqt64, 
         __syncthreads();
     }
     if (t == 0) count_out[item] = base;
-}
-
-// ---------------------------------------------------------------------------
-// Per row: D = dO . O (fp32) and the base-2 LSE.  16 lanes per row; each
-// 16-lane group takes PREP_ROWS rows and issues all their loads before
-// using any.  Grid (row blocks, Hq, B): no index division.
-// ---------------------------------------------------------------------------
-constexpr int PREP_ROWS = 4;
-constexpr int PREP_BLOCK_ROWS = 16 * PREP_ROWS; // 256 threads = 16 groups of 16 lanes
-template <int D>
-__global__ __launch_bounds__(256) void k_bwd_prep(BwdParams p) {
-    constexpr int LPR = 16, PER = D / LPR; // lanes per row, elements per lane (8 or 4)
-    typedef uint32_t vec_t __attribute__((ext_vector_type(PER / 2)));
-    const int part = threadIdx.x % LPR, grp = threadIdx.x / LPR;
-    const int h = blockIdx.y, b = blockIdx.z;
-    const int i0 = blockIdx.x * PREP_BLOCK_ROWS + grp * PREP_ROWS;
-    vec_t ov[PREP_ROWS], gv[PREP_ROWS];
-#pragma unroll
-    for (int k = 0; k < PREP_ROWS; ++k) {
-        const int i = min(i0 + k, p.N - 1); // rows past N re-read row N-1, result dropped
-        ov[k] = *reinterpret_cast<const vec_t *>(p.o + b * p.o_sb + h * p.o_sh + int64_t(i) * p.o_sn + PER * part);
-        gv[k] = *reinterpret_cast<const vec_t *>(p.dout + b * p.do_sb + h * p.do_sh + int64_t(i) * p.do_sn +
-                                                 PER * part);
-    }
-#pragma unroll
-    for (int k = 0; k < PREP_ROWS; ++k) {
-        float acc = 0.f;
-#pragma unroll
-        for (int e = 0; e < PER / 2; ++e) {
-            const uint32_t x = ov[k][e], y = gv[k][e];
-            acc += __builtin_bit_cast(float, x << 16) * __builtin_bit_cast(float, y << 16);
-            acc += __builtin_bit_cast(float, x & 0xffff0000u) * __builtin_bit_cast(float, y & 0xffff0000u);
-        }
-#pragma unroll
-        for (int off = 1; off < LPR; off <<= 1) acc += __shfl_xor(acc, off);
-        const int i = i0 + k;
-        if (i < p.N && part == 0) {
-            const int64_t r = (int64_t(b) * p.Hq + h) * p.N + i;
-            p.dvec[r] = acc;
-            const float l = p.lse[r];
-            p.lse2[r] = l == -INFINITY ? INFINITY : l * LOG2E;
-        }
-    }
 }
 
 // ---------------------------------------------------------------------------
@@ -349,12 +307,29 @@ __device__ __forceinline__ void bwd_dq_body(const BwdParams &p) {
     load_frag<D>(p.dout + b * p.do_sb + h * p.do_sh + int64_t(row) * p.do_sn, row_ok, half, gf);
     int lo = 1, hi = 0;
     float lse2 = INFINITY, dd = 0.f;
-    if (row_ok) {
-        lo = p.mask.lo[int64_t(b) * p.N + row];
-        hi = p.mask.hi[int64_t(b) * p.N + row];
-        const int64_t r = (int64_t(b) * p.Hq + h) * p.N + row;
-        lse2 = p.lse2[r];
-        dd = p.dvec[r];
+    {
+        // The row's D = rowsum(dO * O) and base-2 LSE are formed here, from
+        // the dO fragment already in registers and the row of O read in the
+        // same layout, and written for the dK/dV kernel that runs next.
+        bf16x8_t of[C::KSTEPS];
+        load_frag<D>(p.o + b * p.o_sb + h * p.o_sh + int64_t(row) * p.o_sn, row_ok, half, of);
+        float acc = 0.f;
+#pragma unroll
+        for (int s2 = 0; s2 < C::KSTEPS; ++s2)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc = __builtin_fmaf(float(gf[s2][e]), float(of[s2][e]), acc);
+        dd = acc + wave_swap_halves(acc, half);
+        if (row_ok) {
+            lo = p.mask.lo[int64_t(b) * p.N + row];
+            hi = p.mask.hi[int64_t(b) * p.N + row];
+            const int64_t r = (int64_t(b) * p.Hq + h) * p.N + row;
+            const float l = p.lse[r];
+            lse2 = l == -INFINITY ? INFINITY : l * LOG2E;
+            if (half == 0) {
+                p.dvec[r] = dd;
+                p.lse2[r] = lse2;
+            }
+        }
     }
     // Element mask of PARTIAL tiles, as in the forward: key is visible iff
     // key - lo <= hi - lo as unsigned numbers; a row with no visible key
@@ -678,10 +653,7 @@ static hipError_t launch_with_lds(void (*kernel)(BwdParams), int64_t nblocks, si
 template <int D>
 static hipError_t launch_bwd_d(const BwdParams &p, bool softcap, hipStream_t stream) {
     using C = FwdCfg<D>;
-    hipLaunchKernelGGL((k_bwd_prep<D>), dim3(unsigned((p.N + PREP_BLOCK_ROWS - 1) / PREP_BLOCK_ROWS), p.Hq, p.B),
-                       dim3(256), 0, stream, p);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    hipError_t e;
     void (*dq)(BwdParams);
     void (*dkdv)(BwdParams);
     const bool same = p.k_sn == p.v_sn; // K and V DMAs can share their offsets
