@@ -108,9 +108,14 @@ __device__ __forceinline__ void row_interval(const attn_mask_spec &spec, const V
 //   number of rows that touch it.
 // The visited tiles are written in key order with a ballot/popcount
 // compaction.
+// order_direct: the heavy-first order, written here (and k_mask_order not
+// run) when it has a closed form: under a plain causal mask over equal
+// query and key counts, query tile qt visits floor(last row / 64) + 1 key
+// tiles, a count that grows strictly with qt, so the order is the reverse
+// tile order.
 __global__ __launch_bounds__(256) void k_mask_tiles(attn_mask_spec spec, VarlenView vl, int N, int Nk, int nqt,
                                                     int nkt, int32_t *lo_out, int32_t *hi_out, int32_t *count_out,
-                                                    int32_t *list_out) {
+                                                    int32_t *list_out, int32_t *order_direct) {
     __shared__ int32_t s_lo[BLOCK_M], s_hi[BLOCK_M];
     __shared__ int32_t s_diff[257];
     __shared__ int32_t s_wsum[4];
@@ -198,7 +203,10 @@ __global__ __launch_bounds__(256) void k_mask_tiles(attn_mask_spec spec, VarlenV
         base += total;
         __syncthreads(); // s_diff and s_wsum are rewritten by the next round
     }
-    if (t == 0) count_out[item] = base;
+    if (t == 0) {
+        count_out[item] = base;
+        if (order_direct) order_direct[int64_t(b) * nqt + (nqt - 1 - qt)] = qt;
+    }
 }
 
 // One workgroup per batch row: order[b][rank] = query tile, ranked by
@@ -256,10 +264,12 @@ hipError_t launch_mask_build(const attn_mask_spec &spec, const MaskLayout &L, vo
     int32_t *cnt = reinterpret_cast<int32_t *>(base + L.off_count);
     int32_t *list = reinterpret_cast<int32_t *>(base + L.off_list);
     int32_t *order = reinterpret_cast<int32_t *>(base + L.off_order);
+    const uint32_t mask_bits = spec.flags & (ATTN_MASK_CAUSAL | ATTN_MASK_WINDOW | ATTN_MASK_DOCS | ATTN_MASK_NO_SKIP);
+    const bool causal_only = mask_bits == ATTN_MASK_CAUSAL && vl.cu_q == nullptr && L.N == L.Nk;
     hipLaunchKernelGGL(k_mask_tiles, dim3(L.nqt, L.B), dim3(256), 0, stream, spec, vl, L.N, L.Nk, L.nqt, L.nkt,
-                       lo, hi, cnt, list);
+                       lo, hi, cnt, list, causal_only ? order : nullptr);
     hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    if (e != hipSuccess || causal_only) return e;
     const size_t order_lds = L.nqt <= ORDER_LDS_TILES ? 2 * size_t(L.nqt) * sizeof(int32_t) : 0;
     const bool by_doc = (spec.flags & ATTN_MASK_DOCS) || vl.cu_q != nullptr;
     hipLaunchKernelGGL(k_mask_order, dim3(L.B), dim3(1024), order_lds, stream, L.nqt, L.N, by_doc, cnt, lo,
