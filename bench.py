@@ -97,8 +97,8 @@ MEASURED_TRAFFIC = {
     "varlen_gqa32x8_docs_causal_b2_n8192_d128": (
         "k_mask_tiles + k_mask_order + k_attn_fwd_d128",
         ["fwd.hip", "tile.h", "common.h", "../build.py", "mask.hip"],
-        "0f05cc1a2c778ce8ed424ee44c6f777002087d665d305bb06953c97a6865a915",
-        349434813,
+        "b0e43b10366c5b1e028c3f7ac4189ffc2cfa6945442ea44477fe003fbcd55d28",
+        349854851,
         "profiles/attn_fwd_varlen_gqa32x8_docs_b2_n8192_d128.md"),
     "alibi_causal_b8_h32_n4096_d128": (
         "k_attn_fwd_d128_alibi",
@@ -121,8 +121,8 @@ MEASURED_TRAFFIC = {
     "bwd_causal_b8_h32_n4096_d128": (
         "all kernels of one attn_bwd call",
         ["bwd.hip", "tile.h", "common.h", "mask.hip", "../build.py"],
-        "5a8c372ca2a1d4ba486f6354e9a33390f46c0b4bef9fb7078b2d78645e22fd6d",
-        3284686419,
+        "43b774b8bfb2726cddb7538a6bcbf31850ba715ed95577eaed6001944a16e372",
+        3284480928,
         "profiles/k_bwd_d128_causal_b8_h32_n4096_d128.md"),
 }
 
