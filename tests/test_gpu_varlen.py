@@ -108,10 +108,12 @@ def test_packed_documents_match_docs_mask(ea):
     assert torch.equal(l1, l2[0])
 
 
-def test_full_size_packed_documents_sampled(ea):
+def test_full_size_packed_documents(ea):
     # the GQA document workload (2 x 8192 tokens, documents U[256, 4096], 32
-    # query heads over 8 KV heads, d 128) packed into one varlen call,
-    # checked on sampled rows
+    # query heads over 8 KV heads, d 128) packed into one varlen call:
+    # every output equal, bit for bit, to the documents-mask forward of the
+    # same inputs (which the full-size forward test checks on every row
+    # against the oracle), and sampled rows against the varlen oracle
     c = gen.CONFIGS[4]
     q4, k4, v4, docs = gen.fwd_inputs(c["seed"], c["B"], c["Hq"], c["Hkv"], c["N"], c["d"],
                                       c["factor"], docs=True)
@@ -132,3 +134,10 @@ def test_full_size_packed_documents_sampled(ea):
     og = bf16_to_f64(o)[rows[:, 1], rows[:, 0]]
     lg = lse.cpu().numpy()[rows[:, 0], rows[:, 1]]
     compare(og, lg, ro, rl, "full-size packed documents")
+    padded, _ = gen.pad_offsets(docs, N)
+    o2, l2 = ea.fwd(to_dev(q4), to_dev(k4), to_dev(v4), causal=True, scale=scale,
+                    doc_offsets=torch.from_numpy(padded).cuda())
+    torch.cuda.synchronize()
+    B = c["B"]
+    assert torch.equal(o, o2.transpose(1, 2).reshape(B * N, c["Hq"], c["d"])), "packed O differs from the docs mask"
+    assert torch.equal(lse, l2.transpose(0, 1).reshape(c["Hq"], B * N)), "packed LSE differs from the docs mask"
