@@ -45,3 +45,30 @@ def sample_rows(rng, B, H, N, n, must=()):
 
 def scale_for(d):
     return 1.0 / math.sqrt(d)
+
+
+# Backward bound, derived in tests/test_gpu_bwd.py's module docstring: per
+# tensor, max|g - g_ref| <= GRAD_TOL * max|g_ref| + GRAD_ABS.
+GRAD_TOL = 1e-2
+GRAD_ABS = 1e-4
+
+
+def compare_grads(got, ref, lse, what):
+    """got, ref: (dq, dk, dv); lse: the GPU forward's LSE (rows at -inf see
+    no key, so their dQ must be exactly zero, as must dK and dV of keys that
+    no row sees, i.e. whose reference dV row is zero)."""
+    empty_rows = np.isneginf(np.asarray(lse))
+    unseen = ~np.asarray(ref[2]).any(axis=-1)
+    assert not np.asarray(got[0])[empty_rows].any(), f"{what}: dq nonzero on a row with no visible key"
+    assert not np.asarray(got[1])[unseen].any(), f"{what}: dk nonzero on a key no row sees"
+    assert not np.asarray(got[2])[unseen].any(), f"{what}: dv nonzero on a key no row sees"
+    errs = []
+    for name, g, r in zip(("dq", "dk", "dv"), got, ref):
+        g = np.asarray(g, dtype=np.float64)
+        assert g.shape == r.shape, (what, name, g.shape, r.shape)
+        assert np.all(np.isfinite(g)), f"{what}: non-finite {name}"
+        mx = float(np.abs(r).max()) if r.size else 0.0
+        err = float(np.abs(g - r).max()) if r.size else 0.0
+        assert err <= GRAD_TOL * mx + GRAD_ABS, f"{what}: {name} max err {err:.3e} vs max|ref| {mx:.3e}"
+        errs.append(err / max(mx, 1e-30))
+    return errs

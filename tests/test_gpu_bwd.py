@@ -27,15 +27,11 @@ import pytest
 
 import attn_inputs as gen
 import oracle
-from tests.helpers import bf16_to_f64, to_dev
+from tests.helpers import bf16_to_f64, compare_grads, to_dev
 
 pytestmark = pytest.mark.gpu
 
 torch = pytest.importorskip("torch")
-
-GRAD_TOL = 1e-2
-GRAD_ABS = 1e-4
-
 
 @pytest.fixture(scope="module")
 def ea():
@@ -49,27 +45,6 @@ def ea():
 def _grad_inputs(seed, B, Hq, Hkv, N, d, factor):
     q, k, v, _ = gen.fwd_inputs(seed, B, Hq, Hkv, N, d, factor)
     return q, k, v, gen.dout_input(seed + 7919, B, Hq, N, d)
-
-
-def compare_grads(got, ref, lse, what):
-    """got, ref: (dq, dk, dv); lse: the GPU forward's LSE (rows at -inf see
-    no key, so their dQ must be exactly zero, as must dK and dV of keys that
-    no row sees, i.e. whose reference dV row is zero)."""
-    empty_rows = np.isneginf(np.asarray(lse))
-    unseen = ~np.asarray(ref[2]).any(axis=-1)
-    assert not np.asarray(got[0])[empty_rows].any(), f"{what}: dq nonzero on a row with no visible key"
-    assert not np.asarray(got[1])[unseen].any(), f"{what}: dk nonzero on a key no row sees"
-    assert not np.asarray(got[2])[unseen].any(), f"{what}: dv nonzero on a key no row sees"
-    errs = []
-    for name, g, r in zip(("dq", "dk", "dv"), got, ref):
-        g = np.asarray(g, dtype=np.float64)
-        assert g.shape == r.shape, (what, name, g.shape, r.shape)
-        assert np.all(np.isfinite(g)), f"{what}: non-finite {name}"
-        mx = float(np.abs(r).max()) if r.size else 0.0
-        err = float(np.abs(g - r).max()) if r.size else 0.0
-        assert err <= GRAD_TOL * mx + GRAD_ABS, f"{what}: {name} max err {err:.3e} vs max|ref| {mx:.3e}"
-        errs.append(err / max(mx, 1e-30))
-    return errs
 
 
 def run_case(ea, *, B, Hq, Hkv, N, d, seed, factor=1.0, causal=False, window=None,

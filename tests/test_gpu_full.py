@@ -10,8 +10,7 @@ import pytest
 import attn_inputs as gen
 import bench
 import oracle
-from tests.helpers import bf16_to_f64, compare, to_dev
-from tests.test_gpu_bwd import compare_grads
+from tests.helpers import bf16_to_f64, compare, compare_grads, to_dev
 
 pytestmark = pytest.mark.gpu
 
